@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs shaped like the pages' attention workloads.
+
+This module holds input generation only: shapes, seeds, distributions and
+block masks.  It contains none of the attention arithmetic, so the HIP path,
+the CPU oracle, the tests and the benchmark can all draw their inputs from it
+without sharing any part of the method.
+
+Recipe (the same for every workload):
+  * a CPU ``torch.Generator`` seeded with the workload's seed draws Q, K, V
+    (then dO for backward workloads) in that order with ``torch.randn`` in
+    float32, shape (B, H, N, d);
+  * each tensor is multiplied by ``sigma`` and then rounded to the workload
+    dtype (round-to-nearest-even for bfloat16);
+  * block masks are uint8 with the diagonal always on and a fixed count of
+    off-diagonal blocks, round(frac * (T*T - T)), drawn without replacement by
+    ``numpy.random.default_rng(seed)``.
+
+Shapes follow the pages' workloads: a small fp32 single head (the simplified
+one-row-per-block kernel of the page "FlashAttention：在线 softmax 与
+IO-aware 注意力" runs fp32 at d = 64), the GPT-2 head shape at sequence 1K
+(d = 64), long-sequence d = 128 heads at 8K and 4K, and a 16K block-sparse
+setting like the long-range experiments of the page "FlashAttention:
+IOを意識した高速かつメモリ効率の高い厳密なアテンション".  Synthetic
+Gaussian tensors stand in for any dataset; none is used.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+__all__ = ["WORKLOADS", "workload", "make_inputs", "block_mask",
+           "workload_mask"]
+
+
+def _w(name, B, H, N, d, dtype, causal, passes, seed, sigma=1.0,
+       sparse=None):
+    return dict(name=name, B=B, H=H, N=N, d=d, dtype=dtype, causal=causal,
+                passes=passes, seed=seed, sigma=sigma,
+                scale=1.0 / math.sqrt(d), sparse=sparse)
+
+
+# The five workloads, keyed by a stable name.
+WORKLOADS = {
+    "fp32_1x1x256x64": _w("fp32_1x1x256x64", 1, 1, 256, 64, "f32",
+                          (False,), ("fwd",), seed=1),
+    "gpt2_8x16x1024x64": _w("gpt2_8x16x1024x64", 8, 16, 1024, 64, "bf16",
+                            (False, True), ("fwd",), seed=2),
+    "causal_2x32x8192x128": _w("causal_2x32x8192x128", 2, 32, 8192, 128,
+                               "bf16", (True,), ("fwd", "bwd"), seed=3,
+                               sigma=0.5),
+    "bwd_4x16x4096x128": _w("bwd_4x16x4096x128", 4, 16, 4096, 128, "bf16",
+                            (True,), ("fwd", "bwd"), seed=4),
+    "sparse_1x16x16384x64": _w("sparse_1x16x16384x64", 1, 16, 16384, 64,
+                               "bf16", (False,), ("fwd",), seed=5,
+                               sparse=dict(block=128, frac=0.25, seed=5)),
+}
+
+
+def workload(name):
+    return dict(WORKLOADS[name])
+
+
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def make_inputs(B, H, N, d, seed, sigma=1.0, dtype="bf16", with_do=False,
+                device="cpu"):
+    """Q, K, V (and dO) drawn as described in the module docstring.
+
+    Returns a dict of tensors on ``device`` in the requested dtype.
+    """
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    names = ("q", "k", "v", "do") if with_do else ("q", "k", "v")
+    out = {}
+    for n in names:
+        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x = x * sigma
+        out[n] = x.to(_DTYPES[dtype]).to(device)
+    return out
+
+
+def block_mask(t_m, t_n, seed, frac, diagonal=True):
+    """uint8 block mask of shape (t_m, t_n).
+
+    With ``diagonal`` the blocks (i, i) are always on; then
+    round(frac * number of other blocks) of the other blocks are switched on,
+    chosen uniformly without replacement.
+    """
+    m = np.zeros((t_m, t_n), dtype=np.uint8)
+    idx = np.arange(t_m * t_n)
+    if diagonal:
+        diag = [i * t_n + i for i in range(min(t_m, t_n))]
+        m.flat[diag] = 1
+        idx = np.setdiff1d(idx, diag)
+    count = int(round(frac * idx.size))
+    rng = np.random.default_rng(seed)
+    m.flat[rng.choice(idx, count, replace=False)] = 1
+    return m
+
+
+def workload_mask(w):
+    """The block mask of a block-sparse workload (None for dense ones)."""
+    sp = w.get("sparse")
+    if not sp:
+        return None
+    t = -(-w["N"] // sp["block"])
+    return block_mask(t, t, sp["seed"], sp["frac"])
+
+
+def workload_inputs(name, with_do=None, device="cpu"):
+    """Inputs of a named workload (dO included for backward workloads)."""
+    w = WORKLOADS[name]
+    if with_do is None:
+        with_do = "bwd" in w["passes"]
+    return make_inputs(w["B"], w["H"], w["N"], w["d"], w["seed"], w["sigma"],
+                       w["dtype"], with_do, device)

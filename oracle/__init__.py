@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for exact attention — test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  It shares no code with the HIP library.
+"""
+
+from .attention import (  # noqa: F401
+    attention_bwd,
+    attention_bwd_head,
+    attention_fwd,
+    attention_fwd_head,
+    causal_tiles_visited,
+    expand_block_mask,
+    tiled_fwd_fa1_head,
+    tiled_fwd_head,
+    visible,
+)

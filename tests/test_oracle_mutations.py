@@ -1,0 +1,90 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is the oracle's source with one plausible slip (a dropped term, a
+wrong sign or index, a transposed operand).  The mutated source is executed
+as a throw-away module on the CPU and run through the pin checks of
+``oracle_pins``; the test passes when some check rejects it.  This shows that
+the pins constrain every part of the oracle, not only that the oracle passes
+them.
+"""
+
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle",
+                        "attention.py")
+
+# (description, original text, replacement, which occurrence)
+MUTATIONS = [
+    ("fwd: scale dropped", "S = scale * (q[r] @ k.T)", "S = (q[r] @ k.T)", 0),
+    ("bwd: scale dropped in recomputed S", "S = scale * (q[r] @ k.T)",
+     "S = (q[r] @ k.T)", 1),
+    ("fwd: P transposed in O = P V", "O[c0:c0 + r.size] = P @ v",
+     "O[c0:c0 + r.size] = P.T @ v", 0),
+    ("causal: strict inequality", "cols[None, :] <= rows[:, None]",
+     "cols[None, :] < rows[:, None]", 0),
+    ("causal: reversed", "cols[None, :] <= rows[:, None]",
+     "cols[None, :] >= rows[:, None]", 0),
+    ("block mask: indices swapped",
+     "bm[rows[:, None] // block_m, cols[None, :] // block_n]",
+     "bm[cols[None, :] // block_n, rows[:, None] // block_m]", 0),
+    ("LSE: max term dropped", "m + np.log(l))", "np.log(l))", 0),
+    ("softmax: not normalised", "P = E / np.where(empty, 1.0, l)[:, None]",
+     "P = E", 0),
+    ("softmax: max added instead of subtracted",
+     "E = np.exp(S - m_shift[:, None])", "E = np.exp(S + m_shift[:, None])",
+     0),
+    ("bwd: dV = P dO", "dv += P.T @ do[r]", "dv += P @ do[r]", 0),
+    ("bwd: dP sign", "dP = do[r] @ v.T", "dP = -do[r] @ v.T", 0),
+    ("bwd: D term dropped", "dS = P * (dP - D[:, None])", "dS = P * dP", 0),
+    ("bwd: D over the wrong axis", "D = (P * dP).sum(axis=1)",
+     "D = (P * dP).sum(axis=0)", 0),
+    ("bwd: dQ with dS transposed", "dq[r] = scale * (dS @ k)",
+     "dq[r] = scale * (dS.T @ k)", 0),
+    ("bwd: dK without transpose", "dk += scale * (dS.T @ q[r])",
+     "dk += scale * (dS @ q[r])", 0),
+    ("bwd: dK scale dropped", "dk += scale * (dS.T @ q[r])",
+     "dk += (dS.T @ q[r])", 0),
+    ("tiled: alpha inverted", "alpha = np.exp(m - shift)",
+     "alpha = np.exp(shift - m)", 0),
+    ("tiled: accumulator not rescaled", "a = a_scaled + Pt @ v[j0:j1]",
+     "a = a + Pt @ v[j0:j1]", 0),
+    ("tiled: exp-sum not rescaled", "l = l_scaled + Pt.sum(axis=1)",
+     "l = l + Pt.sum(axis=1)", 0),
+    ("tiled: causal block skip too eager",
+     "return (not causal) or j0 <= i1 - 1", "return (not causal) or j0 <= i0",
+     0),
+    ("FA1: old sum not rescaled", "l_new = c_old * l + c_blk * l_blk",
+     "l_new = l + c_blk * l_blk", 0),
+    ("FA1: output not un-normalised",
+     "num = (l * c_old)[:, None] * o", "num = c_old[:, None] * o", 0),
+]
+
+
+def _mutant(old, new, occurrence):
+    with open(SRC_PATH) as f:
+        src = f.read()
+    parts = src.split(old)
+    assert len(parts) - 1 > occurrence, f"pattern not in oracle: {old!r}"
+    mutated = old.join(parts[:occurrence + 1]) + new + old.join(
+        parts[occurrence + 1:])
+    assert mutated != src
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(mutated, "<oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("desc,old,new,occ", MUTATIONS,
+                         ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(desc, old, new, occ):
+    mod = _mutant(old, new, occ)
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:       # AssertionError, or a crash on bad shapes
+            return
+    pytest.fail(f"no pin catches the planted mistake: {desc}")
