@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one forward and one backward pass (preprocess, dK/dV pass, dQ
+pass) of bf16 causal attention at B=2, H=32, N=8192, d=128 on synthetic
+inputs already resident in device memory.  Prints one JSON line.
+
+  value      whole-step throughput in TFLOP/s (forward 4*B*H*N^2*d/2 plus
+             backward 2.5x that, divided by the measured step time)
+  roofline   the kernel with the largest share of the step time: its
+             algorithmic FLOP per launch over its mean launch time (HIP events
+             on the launch stream), against the dense bf16 MFMA peak
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+             (whole heads, forward + backward), as a reference only
+
+Options: --gpus N (only 1 is supported), --steps K, --warmup W,
+--no-cpu-baseline, --workload NAME (any backward-capable workload),
+--calib-copy-mb M (launch one plain device copy of M MiB before timing, for
+hardware-counter calibration), --all (also time every other workload and
+print one extra JSON line per workload; not part of the driver contract).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4096 x 2.4 GHz)
+PEAK_F32_TFLOPS = 157.3
+METRIC = "attention fwd/bwd TFLOP/s (bf16, N=8192 d=128 causal) + % MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_io_aware_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def time_workload(name, steps, warmup, calib_mb=0):
+    import torch
+
+    from exact_io_aware_amd import fa, workloads
+
+    w = workloads.workload(name)
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"][-1]
+    dev = torch.device("cuda:0")
+    x = workloads.workload_inputs(name, with_do=True, device=dev)
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    scale = w["scale"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(q.shape, **f32) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if calib_mb:
+        src = torch.ones(calib_mb * (1 << 20) // 4, **f32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    ev = {n: [] for n in names}
+
+    def rec():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record):
+        marks = [rec()] if record else None
+        fa.fa_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        if record:
+            marks.append(rec())
+        fa.fa_bwd_preprocess(o, do, lse, ws)
+        if record:
+            marks.append(rec())
+        fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale=scale, causal=causal)
+        if record:
+            marks.append(rec())
+        fa.fa_bwd_dq(q, k, v, do, ws, dq, scale=scale, causal=causal)
+        if record:
+            marks.append(rec())
+            for i, n in enumerate(names):
+                ev[n].append((marks[i], marks[i + 1]))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = rec()
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    t1 = rec()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / steps
+               for n in names}
+    ff = fwd_flops(B, H, N, d, causal)
+    alg = {"fwd": ff, "bwd_preprocess": 0.0, "bwd_dkdv": 0.8 * 2.5 * ff,
+           "bwd_dq": 0.2 * 2.5 * ff}
+    return dict(w=w, B=B, H=H, N=N, d=d, causal=causal, ms_step=ms_step,
+                wall=wall, kern_ms=kern_ms, fwd_flops=ff, bwd_flops=2.5 * ff,
+                alg=alg)
+
+
+def time_forward_only(name, steps, warmup):
+    """Per-workload forward timing (used by --all)."""
+    import torch
+
+    from exact_io_aware_amd import fa, workloads
+
+    w = workloads.workload(name)
+    dev = torch.device("cuda:0")
+    x = workloads.workload_inputs(name, with_do=False, device=dev)
+    mask = workloads.workload_mask(w)
+    mask_t = torch.from_numpy(mask).to(dev) if mask is not None else None
+    out = []
+    for causal in w["causal"]:
+        def run():
+            if mask_t is not None:
+                fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], mask_t,
+                                      scale=w["scale"], causal=causal)
+            else:
+                fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"],
+                          causal=causal)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            times.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+        if mask is not None:
+            flops = 4.0 * w["d"] * 128 * 128 * float(mask.sum()) * w["B"] * w["H"]
+        else:
+            flops = fwd_flops(w["B"], w["H"], w["N"], w["d"], causal)
+        tf = flops / (ms * 1e-3) / 1e12
+        peak = PEAK_F32_TFLOPS if w["dtype"] == "f32" else PEAK_BF16_TFLOPS
+        out.append(dict(workload=name, causal=causal, pass_="fwd",
+                        ms_median=ms, tflops=tf, frac_peak=tf / peak))
+    return out
+
+
+def cpu_baseline(name, budget_s=12.0, max_heads=8):
+    """The fp64 oracle (forward + backward of whole heads) on host cores."""
+    import numpy as np
+
+    import oracle
+    from exact_io_aware_amd import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    w = workloads.workload(name)
+    x = workloads.workload_inputs(name, with_do=True)
+    causal = w["causal"][-1]
+    heads, t_total = 0, 0.0
+    for b in range(w["B"]):
+        for hh in range(w["H"]):
+            q, k, v, do = (x[n][b, hh].double().numpy() for n in
+                           ("q", "k", "v", "do"))
+            t0 = time.perf_counter()
+            oracle.attention_fwd_head(q, k, v, w["scale"], causal)
+            oracle.attention_bwd_head(q, k, v, do, w["scale"], causal)
+            t_total += time.perf_counter() - t0
+            heads += 1
+            if t_total >= budget_s or heads >= max_heads:
+                break
+        if t_total >= budget_s or heads >= max_heads:
+            break
+    flops = 3.5 * fwd_flops(1, 1, w["N"], w["d"], causal) * heads
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"{heads} whole heads (b,h) of {name}, forward + "
+                       f"backward, fp64 NumPy materialising S and P "
+                       f"(full N^2 even where causal), {t_total:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_2x32x8192x128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0)
+    ap.add_argument("--all", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this "
+              "build has no multi-GPU path; the attention kernels shard by "
+              "(batch, head) with no exchange, so each GPU would run this same "
+              "single-GPU step on its share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from exact_io_aware_amd import fa
+    fa.library()
+
+    r = time_workload(args.workload, args.steps, args.warmup,
+                      args.calib_copy_mb)
+    B, H, N, d = r["B"], r["H"], r["N"], r["d"]
+    step_flops = r["fwd_flops"] + r["bwd_flops"]
+    value = step_flops / (r["ms_step"] * 1e-3) / 1e12
+    km = r["kern_ms"]
+    fwd_tf = r["fwd_flops"] / (km["fwd"] * 1e-3) / 1e12
+    bwd_ms = km["bwd_preprocess"] + km["bwd_dkdv"] + km["bwd_dq"]
+    bwd_tf = r["bwd_flops"] / (bwd_ms * 1e-3) / 1e12
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: km[n])
+    achieved = r["alg"][dom] / (km[dom] * 1e-3) / 1e12
+    kname = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+             "bwd_dq": "bwd_dq_kernel"}[dom]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d,
+                   "causal": bool(r["causal"]), "step": "fwd+bwd",
+                   "seed": r["w"]["seed"], "sigma": r["w"]["sigma"]},
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        "step_frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in km.items()},
+        "roofline": {
+            "kernel": kname,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(kname, args.workload),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    if args.all:
+        from exact_io_aware_amd import workloads
+        for name in workloads.WORKLOADS:
+            for res in time_forward_only(name, max(args.steps, 20), 3):
+                print(json.dumps(res), flush=True)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+// C-ABI entry points (declared in include/fa.h): argument validation and
+// dispatch to the HIP kernels.  Every check runs before any HIP call, so a
+// rejected call enqueues nothing and touches no device state.
+#include <math.h>
+#include <stdint.h>
+
+#include <limits>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxN = (int64_t)1 << 30;
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Checks shared by every entry point that takes a problem shape.  Sets
+// *empty when there is nothing to compute.
+fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                      bool* empty, int64_t* bh) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) {
+    *bh = 0;
+    return FA_OK;
+  }
+  if (N > kMaxN) return FA_ERR_SHAPE;
+  if (B > std::numeric_limits<int64_t>::max() / H) return FA_ERR_SHAPE;
+  const int64_t bh_ = B * H;
+  // Every element offset must fit in int64 and every grid in int32:
+  // at most 2^31 - 1 workgroups of >= 64 rows.
+  if (bh_ > ((int64_t)1 << 62) / (N * d)) return FA_ERR_SHAPE;
+  if (bh_ * ((N + 63) / 64) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+  *bh = bh_;
+  return FA_OK;
+}
+
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
+
+size_t ws_rows(int64_t bh, int64_t n) {
+  // Two float arrays of bh*n rows, the second starting 256-byte aligned.
+  return (size_t)(((bh * n) + 63) / 64 * 64);
+}
+
+size_t ws_bytes(int64_t bh, int64_t n) { return 2 * ws_rows(bh, n) * 4; }
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                     fa_dtype dt, float scale, int causal, const uint8_t* mask,
+                     int64_t block_m, int64_t block_n, bool sparse_call,
+                     void* stream) {
+  bool empty = false;
+  int64_t bh = 0;
+  fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
+  if (st != FA_OK) return st;
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  if (sparse_call) {
+    if (block_m <= 0 || block_n <= 0 || block_m % 128 != 0 ||
+        block_n % 128 != 0 || block_m > kMaxN || block_n > kMaxN) {
+      return FA_ERR_MASK;
+    }
+  }
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(lse, 4)) {
+    return FA_ERR_ALIGN;
+  }
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = bh;
+  a.n = (int)N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.mask = sparse_call ? mask : nullptr;
+  a.block_m = (int)(sparse_call ? block_m : 128);
+  a.block_n = (int)(sparse_call ? block_n : 128);
+  a.mask_cols = (int)((N + a.block_n - 1) / a.block_n);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(dt == FA_BF16 ? fa::launch_fwd_bf16(a, s)
+                                : fa::launch_fwd_f32(a, s));
+}
+
+// Validation shared by fa_bwd and its passes.  `need` lists which pointers
+// the caller must supply.
+enum : unsigned {
+  NEED_Q = 1u, NEED_K = 2u, NEED_V = 4u, NEED_O = 8u, NEED_DO = 16u,
+  NEED_LSE = 32u, NEED_DQ = 64u, NEED_DK = 128u, NEED_DV = 256u,
+};
+
+fa_status bwd_common(unsigned need, const void* q, const void* k,
+                     const void* v, const void* o, const void* dout,
+                     const float* lse, float* dq, float* dk, float* dv,
+                     const void* workspace, size_t workspace_bytes, int64_t B,
+                     int64_t H, int64_t N, int64_t d, fa_dtype dt, float scale,
+                     bool check_scale, int causal, fa::BwdArgs* out,
+                     bool* empty) {
+  int64_t bh = 0;
+  fa_status st = check_shape(B, H, N, d, dt, empty, &bh);
+  if (st != FA_OK) return st;
+  if (check_scale && !scale_ok(scale)) return FA_ERR_ARG;
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (*empty) return FA_OK;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (int i = 0; i < 9; ++i) {
+    if ((need >> i) & 1u) {
+      if (!ptrs[i]) return FA_ERR_NULL;
+      if (!aligned(ptrs[i], i == 5 ? 4 : 16)) return FA_ERR_ALIGN;  // lse: 4
+    }
+  }
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (workspace_bytes < ws_bytes(bh, N)) return FA_ERR_ARG;
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  float* ws = const_cast<float*>(static_cast<const float*>(workspace));
+  a.ws_d = ws;
+  a.ws_lse2 = ws + ws_rows(bh, N);
+  a.bh = bh;
+  a.n = (int)N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  *out = a;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
+                 float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                 fa_dtype dt, float scale, int causal, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, dt, scale, causal, nullptr,
+                    128, 128, false, stream);
+}
+
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, dt, scale, causal, mask,
+                    block_m, block_n, true, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  bool empty = false;
+  int64_t bh = 0;
+  if (check_shape(B, H, N, d, FA_BF16, &empty, &bh) != FA_OK || empty) return 0;
+  return ws_bytes(bh, N);
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d,
+                            fa_dtype dt, void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(NEED_O | NEED_DO | NEED_LSE, nullptr, nullptr,
+                            nullptr, o, dout, lse, nullptr, nullptr, nullptr,
+                            workspace, workspace_bytes, B, H, N, d, dt, 1.f,
+                            false, 0, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  return from_hip(fa::launch_bwd_preprocess(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v,
+                      const void* dout, float* dk, float* dv,
+                      const void* workspace, size_t workspace_bytes,
+                      int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                      float scale, int causal, void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(NEED_Q | NEED_K | NEED_V | NEED_DO | NEED_DK | NEED_DV,
+                            q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  return from_hip(fa::launch_bwd_dkdv(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
+                    const void* dout, float* dq, const void* workspace,
+                    size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                    int64_t d, fa_dtype dt, float scale, int causal,
+                    void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(NEED_Q | NEED_K | NEED_V | NEED_DO | NEED_DQ, q, k,
+                            v, nullptr, dout, nullptr, dq, nullptr, nullptr,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  return from_hip(fa::launch_bwd_dq(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, float* dq, float* dk,
+                 float* dv, void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                 float scale, int causal, void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(fa::launch_bwd_preprocess(a, s));
+  if (st != FA_OK) return st;
+  st = from_hip(fa::launch_bwd_dkdv(a, s));
+  if (st != FA_OK) return st;
+  return from_hip(fa::launch_bwd_dq(a, s));
+}
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or overflowing size";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; backward needs bf16";
+    case FA_ERR_MASK:
+      return "FA_ERR_MASK: block sizes must be positive multiples of 128";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointer not 16-byte aligned";
+    case FA_ERR_ARG:
+      return "FA_ERR_ARG: scale must be finite and > 0, workspace large enough";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_version(void) { return "exact_io_aware_amd 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,463 @@
+// Backward pass by recomputation, bf16 inputs, fp32 accumulation, gfx950.
+//
+// Pages cited (titles as published):
+//   [TLDR]   "FlashAttention：メモリ効率的なアテンション計算" (tech-tldr.com)
+//   [XYZ]    "FlashAttention: IOを意識した高速かつメモリ効率の高い厳密な
+//            アテンション" (xyznot.com)
+//   [REAPER] "3 · FlashAttention" (mkdocs.reaper.mx, chapter 3)
+//   [Q67]    "FlashAttention：在线 softmax 与 IO-aware 注意力" (quant67.com)
+//
+// The forward saves only O and one logsumexp per row; the backward rebuilds
+// each score/probability tile on chip from Q, K and that statistic instead
+// of reading a stored N x N matrix ([TLDR] backward section; [XYZ] key
+// ideas; [REAPER] 3.4; [Q67] section 5).  The gradient formulas are the
+// chain rule applied to O = softmax(scale Q K^T) V:
+//   P = exp(scale q_i.k_j - lse_i),  D_i = sum_c dO_ic O_ic,
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//   dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Three kernels, no atomics:
+//   preprocess : D_i and lse_i * log2(e) per row (a streaming pass).
+//   dkdv       : a workgroup owns 128 keys (32 per wave, K and V held in
+//                registers) and sweeps the query tiles, accumulating dK^T
+//                and dV^T in registers; each is written once.
+//   dq         : a workgroup owns 128 queries (32 per wave, Q and dO held in
+//                registers) and sweeps the key tiles, accumulating dQ^T.
+// All four contractions per tile pair run on v_mfma_f32_32x32x16_bf16.  The
+// dkdv pass computes S = Q K^T so that each lane owns one key (the N index
+// of the D layout); P and dS then already have the B-operand layout for the
+// contractions over queries, and only Q and dO need a transposed copy in
+// LDS.  The dq pass computes S^T = K Q^T (lane = query) for the same reason
+// and needs a transposed copy of K.  Causal key/query tiles that are fully
+// masked are skipped ([REAPER], causal-mask question).
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) {
+  return __uint_as_float(u << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t u) {
+  return __uint_as_float(u & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------
+// preprocess: D_i = sum_c dO_ic * O_ic, lse2_i = lse_i * log2(e)
+// (+inf for rows whose forward saw no key, so that every rebuilt
+// probability of that row is exactly 0).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_pre_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
+                    const float* __restrict__ lse, float* __restrict__ ws_d,
+                    float* __restrict__ ws_lse2, int64_t rows) {
+  constexpr int TPR = D / 8;  // 16-byte chunks per row
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
+      acc = fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (part == 0 && row < rows) {
+    ws_d[row] = acc;
+    const float L = lse[row];
+    ws_lse2[row] = (L == -INFINITY) ? INFINITY : L * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv pass
+// ---------------------------------------------------------------------------
+template <int D>
+struct KVTile {
+  static constexpr int NW = 4;
+  static constexpr int BCK = 32 * NW;                 // keys per workgroup
+  static constexpr int BRQ = (D == 128) ? 64 : 128;   // queries per LDS tile
+  static constexpr int KS = D / 16;
+  static constexpr int QB = BRQ / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int ROW = D * 2;                   // row-major row bytes
+  static constexpr int TROW = BRQ * 2;                // transposed row bytes
+  static constexpr int T_BYTES = BRQ * ROW;           // == D * TROW
+  // stage layout: Q | Q^T | dO | dO^T | lse2[BRQ] | D[BRQ]
+  static constexpr int OFF_QT = T_BYTES;
+  static constexpr int OFF_DO = 2 * T_BYTES;
+  static constexpr int OFF_DOT = 3 * T_BYTES;
+  static constexpr int OFF_L = 4 * T_BYTES;
+  static constexpr int OFF_D = OFF_L + BRQ * 4;
+  static constexpr int STAGE = OFF_D + BRQ * 4;
+  static_assert((BRQ / 4) * (D / 8) == 256, "one 4x8 unit per thread");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                     const float* __restrict__ ws_d,
+                     const float* __restrict__ ws_lse2, float* __restrict__ dK,
+                     float* __restrict__ dV, int n, int n_ktiles, int total,
+                     float c_log2, float scale) {
+  using T = KVTile<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  const int head = lid / n_ktiles;
+  const int k0 = (lid % n_ktiles) * T::BCK;  // early key tiles are the heavy ones
+  const int64_t hoff = (int64_t)head * n * D;
+  const int64_t roff = (int64_t)head * n;
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+
+  // K and V as B operands (lane = key, slots = 8 consecutive d).
+  bf16x8 kf[T::KS], vf[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    kf[ks] = as_bf16x8(load_row16(K + hoff, key, n, D, ks * 16 + h * 8));
+    vf[ks] = as_bf16x8(load_row16(V + hoff, key, n, D, ks * 16 + h * 8));
+  }
+  f32x16 adk[T::DB], adv[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    adk[db] = zero16();
+    adv[db] = zero16();
+  }
+
+  const int n_qt = (n + T::BRQ - 1) / T::BRQ;
+  const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
+
+  const int dg = tid % (D / 8);
+  const int qg = tid / (D / 8);
+  u32x4 qpre[4], dopre[4];
+  float lpre = 0.f, dpre = 0.f;
+  auto load_tile = [&](int qt) {
+    const int qb0 = qt * T::BRQ;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qpre[r] = load_row16(Q + hoff, qb0 + qg * 4 + r, n, D, dg * 8);
+      dopre[r] = load_row16(dO + hoff, qb0 + qg * 4 + r, n, D, dg * 8);
+    }
+    if (tid < T::BRQ) {
+      const int row = qb0 + tid;
+      lpre = (row < n) ? ws_lse2[roff + row] : INFINITY;
+      dpre = (row < n) ? ws_d[roff + row] : 0.f;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* st = smem + stage * T::STAGE;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<u32x4*>(st + lds_off<T::ROW>(qg * 4 + r, dg)) = qpre[r];
+      *reinterpret_cast<u32x4*>(st + T::OFF_DO + lds_off<T::ROW>(qg * 4 + r, dg)) =
+          dopre[r];
+    }
+    const int pos = (qg >> 2) * 16 + perm_run(qg & 3) * 4;
+    u32x2 tr[8];
+    transpose4x8(qpre, tr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      *reinterpret_cast<u32x2*>(st + T::OFF_QT +
+                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
+                                (pos & 7) * 2) = tr[e];
+    }
+    transpose4x8(dopre, tr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      *reinterpret_cast<u32x2*>(st + T::OFF_DOT +
+                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
+                                (pos & 7) * 2) = tr[e];
+    }
+    if (tid < T::BRQ) {
+      reinterpret_cast<float*>(st + T::OFF_L)[tid] = lpre;
+      reinterpret_cast<float*>(st + T::OFF_D)[tid] = dpre;
+    }
+  };
+
+  int stage = 0;
+  if (qt_begin < n_qt) load_tile(qt_begin);
+  for (int qt = qt_begin; qt < n_qt; ++qt) {
+    store_tile(stage);
+    __syncthreads();
+    if (qt + 1 < n_qt) load_tile(qt + 1);
+    const unsigned char* st = smem + stage * T::STAGE;
+    const float* sL = reinterpret_cast<const float*>(st + T::OFF_L);
+    const float* sD = reinterpret_cast<const float*>(st + T::OFF_D);
+#pragma unroll
+    for (int qb = 0; qb < T::QB; ++qb) {
+      const int qq0 = qt * T::BRQ + qb * 32;
+      if (CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
+      // S = Q K^T and dP = dO V^T (M = query, N = key).
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const int off = lds_off<T::ROW>(qb * 32 + l32, ks * 2 + h);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(st + off);
+        const bf16x8 ado = *reinterpret_cast<const bf16x8*>(st + T::OFF_DO + off);
+        s = mfma32(aq, kf[ks], s);
+        dp = mfma32(ado, vf[ks], dp);
+      }
+      // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.
+      const bool need_mask = CAUSAL && qq0 < kw0 + 31;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L = *reinterpret_cast<const f32x4*>(sL + qb * 32 + g * 8 + h * 4);
+        const f32x4 Dv = *reinterpret_cast<const f32x4*>(sD + qb * 32 + g * 8 + h * 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = 4 * g + t;
+          float p = fast_exp2(fmaf(s[i], c_log2, -L[t]));
+          if (need_mask && qq0 + g * 8 + h * 4 + t < key) p = 0.f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - Dv[t]);
+        }
+      }
+      const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
+      const bf16x8 sf0 = pack8(dp, 0), sf1 = pack8(dp, 1);
+      // dV^T += dO^T P and dK^T += Q^T dS (M = d, N = key, K = query).
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int o0 = lds_off<T::TROW>(db * 32 + l32, (qb * 2) * 2 + h);
+        const int o1 = lds_off<T::TROW>(db * 32 + l32, (qb * 2 + 1) * 2 + h);
+        adv[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_DOT + o0), pf0, adv[db]);
+        adv[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_DOT + o1), pf1, adv[db]);
+        adk[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_QT + o0), sf0, adk[db]);
+        adk[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_QT + o1), sf1, adk[db]);
+      }
+    }
+    stage ^= 1;
+  }
+
+  // D layout of dK^T / dV^T: lane = key, register i -> d = db*32 + (i/4)*8 + h*4 + i%4.
+  if (key < n) {
+    float* dkr = dK + hoff + (int64_t)key * D;
+    float* dvr = dV + hoff + (int64_t)key * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = db * 32 + g * 8 + h * 4;
+        f32x4 xk = {adk[db][4 * g] * scale, adk[db][4 * g + 1] * scale,
+                    adk[db][4 * g + 2] * scale, adk[db][4 * g + 3] * scale};
+        f32x4 xv = {adv[db][4 * g], adv[db][4 * g + 1], adv[db][4 * g + 2],
+                    adv[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dkr + c) = xk;
+        *reinterpret_cast<f32x4*>(dvr + c) = xv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq pass
+// ---------------------------------------------------------------------------
+template <int D>
+struct QTile {
+  static constexpr int NW = 4;
+  static constexpr int BRQ = 32 * NW;                 // queries per workgroup
+  static constexpr int BCK = (D == 128) ? 64 : 128;   // keys per LDS tile
+  static constexpr int KS = D / 16;
+  static constexpr int KB = BCK / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int ROW = D * 2;
+  static constexpr int TROW = BCK * 2;
+  static constexpr int T_BYTES = BCK * ROW;
+  // stage layout: K | K^T | V
+  static constexpr int OFF_KT = T_BYTES;
+  static constexpr int OFF_V = 2 * T_BYTES;
+  static constexpr int STAGE = 3 * T_BYTES;
+  static_assert((BCK / 4) * (D / 8) == 256, "one 4x8 unit per thread");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                   const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                   const float* __restrict__ ws_d,
+                   const float* __restrict__ ws_lse2, float* __restrict__ dQ,
+                   int n, int n_qtiles, int total, float c_log2, float scale) {
+  using T = QTile<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  const int head = lid / n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  const int q0 = qt * T::BRQ;
+  const int64_t hoff = (int64_t)head * n * D;
+  const int qw0 = q0 + 32 * w;
+  const int qrow = qw0 + l32;
+
+  bf16x8 qf[T::KS], dof[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    qf[ks] = as_bf16x8(load_row16(Q + hoff, qrow, n, D, ks * 16 + h * 8));
+    dof[ks] = as_bf16x8(load_row16(dO + hoff, qrow, n, D, ks * 16 + h * 8));
+  }
+  const float lrow = (qrow < n) ? ws_lse2[(int64_t)head * n + qrow] : INFINITY;
+  const float drow = (qrow < n) ? ws_d[(int64_t)head * n + qrow] : 0.f;
+
+  f32x16 adq[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) adq[db] = zero16();
+
+  const int n_kt = (n + T::BCK - 1) / T::BCK;
+  int kt_end = n_kt;
+  if (CAUSAL) kt_end = min(n_kt, (min(q0 + T::BRQ, n) - 1) / T::BCK + 1);
+
+  const int dg = tid % (D / 8);
+  const int kg = tid / (D / 8);
+  u32x4 kpre[4], vpre[4];
+  auto load_tile = [&](int kt) {
+    const int kb0 = kt * T::BCK;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kpre[r] = load_row16(K + hoff, kb0 + kg * 4 + r, n, D, dg * 8);
+      vpre[r] = load_row16(V + hoff, kb0 + kg * 4 + r, n, D, dg * 8);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* st = smem + stage * T::STAGE;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<u32x4*>(st + lds_off<T::ROW>(kg * 4 + r, dg)) = kpre[r];
+      *reinterpret_cast<u32x4*>(st + T::OFF_V + lds_off<T::ROW>(kg * 4 + r, dg)) =
+          vpre[r];
+    }
+    const int pos = (kg >> 2) * 16 + perm_run(kg & 3) * 4;
+    u32x2 tr[8];
+    transpose4x8(kpre, tr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      *reinterpret_cast<u32x2*>(st + T::OFF_KT +
+                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
+                                (pos & 7) * 2) = tr[e];
+    }
+  };
+
+  int stage = 0;
+  if (kt_end > 0) load_tile(0);
+  for (int kt = 0; kt < kt_end; ++kt) {
+    store_tile(stage);
+    __syncthreads();
+    if (kt + 1 < kt_end) load_tile(kt + 1);
+    const unsigned char* st = smem + stage * T::STAGE;
+    const int kbase = kt * T::BCK;
+    if (!CAUSAL || kbase <= qw0 + 31) {
+      const bool need_mask = CAUSAL && kbase + T::BCK - 1 > qw0;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) {
+          const int off = lds_off<T::ROW>(kb * 32 + l32, ks * 2 + h);
+          s = mfma32(*reinterpret_cast<const bf16x8*>(st + off), qf[ks], s);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_V + off),
+                      dof[ks], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
+          const int kj = kbase + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+          if (need_mask && kj > qrow) p = 0.f;
+          dp[i] = p * (dp[i] - drow);
+        }
+        const bf16x8 sf0 = pack8(dp, 0), sf1 = pack8(dp, 1);
+        // dQ^T += K^T dS^T (M = d, N = query, K = key).
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const int o0 = lds_off<T::TROW>(db * 32 + l32, (kb * 2) * 2 + h);
+          const int o1 = lds_off<T::TROW>(db * 32 + l32, (kb * 2 + 1) * 2 + h);
+          adq[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_KT + o0), sf0, adq[db]);
+          adq[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_KT + o1), sf1, adq[db]);
+        }
+      }
+    }
+    stage ^= 1;
+  }
+
+  if (qrow < n) {
+    float* dqr = dQ + hoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = {adq[db][4 * g] * scale, adq[db][4 * g + 1] * scale,
+                   adq[db][4 * g + 2] * scale, adq[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dqr + db * 32 + g * 8 + h * 4) = x;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = a.bh * a.n;
+  const int per = 256 / (D / 8);
+  const int64_t grid = (rows + per - 1) / per;
+  return launch_kernel(bwd_pre_kernel<D>, dim3((unsigned)grid), dim3(256), s,
+                       (const bf16*)a.o, (const bf16*)a.dout, a.lse, a.ws_d,
+                       a.ws_lse2, rows);
+}
+
+template <int D, bool CAUSAL>
+hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
+  using T = KVTile<D>;
+  const int n_kt = (a.n + T::BCK - 1) / T::BCK;
+  const int total = (int)(a.bh * n_kt);
+  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3(total), dim3(256), s,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.dout, (const float*)a.ws_d,
+                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
+                       a.scale * kLog2e, a.scale);
+}
+
+template <int D, bool CAUSAL>
+hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
+  using T = QTile<D>;
+  const int n_qt = (a.n + T::BRQ - 1) / T::BRQ;
+  const int total = (int)(a.bh * n_qt);
+  return launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3(total), dim3(256), s,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.dout, (const float*)a.ws_d,
+                       (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
+                       a.scale * kLog2e, a.scale);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s) {
+  return a.d == 128 ? pre_t<128>(a, s) : pre_t<64>(a, s);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return a.causal ? dkdv_t<128, true>(a, s) : dkdv_t<128, false>(a, s);
+  return a.causal ? dkdv_t<64, true>(a, s) : dkdv_t<64, false>(a, s);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return a.causal ? dq_t<128, true>(a, s) : dq_t<128, false>(a, s);
+  return a.causal ? dq_t<64, true>(a, s) : dq_t<64, false>(a, s);
+}
+
+}  // namespace fa

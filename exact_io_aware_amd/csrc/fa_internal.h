@@ -1,0 +1,53 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernel files.
+// Not installed; the public interface is include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Forward problem, already validated by the C-ABI layer.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t bh;              // B * H
+  int n;                   // sequence length
+  int d;                   // head dim (64 or 128)
+  float scale;             // > 0
+  int causal;
+  const uint8_t* mask;     // nullptr = dense
+  int mask_cols;           // ceil(n / block_n)
+  int block_m;             // multiple of 128
+  int block_n;             // multiple of 128
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* ws_d;             // B*H*N: rowsum(dO * O)
+  float* ws_lse2;          // B*H*N: lse * log2(e), +inf for empty rows
+  int64_t bh;
+  int n;
+  int d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,226 @@
+"""ctypes binding over the C-ABI library (``include/fa.h``).
+
+Argument marshalling only: each function checks the torch tensors it is
+given, allocates outputs with torch on the inputs' device, and passes raw
+device pointers plus the current HIP stream to the entry point of the same
+name.  Every step of the computation runs in the library's HIP kernels.  If
+the library has not been built, every call raises; there is no fallback.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from . import _build
+
+__all__ = [
+    "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_preprocess",
+    "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
+    "fa_version", "library", "LIB_PATH",
+]
+
+LIB_PATH = _build.LIB_PATH
+FA_F32, FA_BF16 = 0, 1
+FA_ERR_HIP = 6
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def library():
+    """The loaded ctypes library (loaded once; raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP attention library not built ({LIB_PATH} missing); run "
+            "__graft_entry__.build() first. There is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, F, I, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                        ctypes.c_int, ctypes.c_size_t)
+    sigs = {
+        "fa_fwd": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P],
+        "fa_fwd_blocksparse": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
+                               I64, I64, P],
+        "fa_bwd": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F,
+                   I, P],
+        "fa_bwd_preprocess": [P, P, P, P, SZ, I64, I64, I64, I64, I, P],
+        "fa_bwd_dkdv": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I,
+                        P],
+        "fa_bwd_dq": [P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I, P],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    lib.fa_bwd_workspace_bytes.restype = SZ
+    lib.fa_status_str.argtypes = [I]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_str(status):
+    return library().fa_status_str(int(status)).decode()
+
+
+def fa_version():
+    return library().fa_version().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise FAError(status, fa_status_str(status))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _shape4(*ts):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be B x H x N x d")
+    for t in ts:
+        if t.shape != ref.shape:
+            raise ValueError(f"shape mismatch {tuple(t.shape)} vs {tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            raise ValueError("all of Q, K, V (, O, dO) must share one dtype")
+        if t.device != ref.device or t.device.type != "cuda":
+            raise ValueError("tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (d fastest)")
+    return tuple(ref.shape)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """O, LSE = attention(q, k, v); q, k, v are B x H x N x d bf16 or fp32."""
+    B, H, N, d = _shape4(q, k, v)
+    lib = library()
+    o = torch.empty_like(q) if out is None else out
+    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+             if lse is None else lse)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B,
+                          H, N, d, _dtype_code(q), _scale(scale, d),
+                          int(bool(causal)), _stream(q.device)))
+    return o, lse_t
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, block_m=128, block_n=128,
+                       scale=None, causal=False, out=None, lse=None):
+    """Forward over the nonzero blocks of ``block_mask`` only.
+
+    ``block_mask`` is a uint8 (or bool) tensor of shape
+    (ceil(N / block_m), ceil(N / block_n)) on the inputs' device, or None for
+    a dense mask.
+    """
+    B, H, N, d = _shape4(q, k, v)
+    lib = library()
+    mask_t = None
+    if block_mask is not None:
+        rows = -(-N // int(block_m))
+        cols = -(-N // int(block_n))
+        if tuple(block_mask.shape) != (rows, cols):
+            raise ValueError(f"block mask must be {rows} x {cols}, got "
+                             f"{tuple(block_mask.shape)}")
+        if block_mask.device != q.device:
+            raise ValueError("block mask must be on the inputs' device")
+        mask_t = block_mask.to(torch.uint8).contiguous()
+    o = torch.empty_like(q) if out is None else out
+    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+             if lse is None else lse)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_blocksparse(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+            _dtype_code(q), _scale(scale, d), int(bool(causal)),
+            _ptr(mask_t), int(block_m), int(block_n), _stream(q.device)))
+    return o, lse_t
+
+
+def fa_bwd_workspace_bytes(B, H, N, d):
+    return int(library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def _workspace(B, H, N, d, device, workspace):
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
+           dq=None, dk=None, dv=None):
+    """dQ, dK, dV (float32) of L = sum(O * dO), recomputing P from lse."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    lib = library()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(q.shape, **f32) if dk is None else dk
+    dv = torch.empty(q.shape, **f32) if dv is None else dv
+    ws, ws_bytes = _workspace(B, H, N, d, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                          ws_bytes, B, H, N, d, _dtype_code(q),
+                          _scale(scale, d), int(bool(causal)),
+                          _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_bwd_preprocess(o, do, lse, workspace):
+    B, H, N, d = _shape4(o, do)
+    with torch.cuda.device(o.device):
+        _check(library().fa_bwd_preprocess(
+            _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), B, H, N, d,
+            _dtype_code(o), _stream(o.device)))
+
+
+def fa_bwd_dkdv(q, k, v, do, workspace, dk, dv, scale=None, causal=False):
+    B, H, N, d = _shape4(q, k, v, do)
+    with torch.cuda.device(q.device):
+        _check(library().fa_bwd_dkdv(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), B,
+            H, N, d, _dtype_code(q), _scale(scale, d), int(bool(causal)),
+            _stream(q.device)))
+
+
+def fa_bwd_dq(q, k, v, do, workspace, dq, scale=None, causal=False):
+    B, H, N, d = _shape4(q, k, v, do)
+    with torch.cuda.device(q.device):
+        _check(library().fa_bwd_dq(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), B, H, N, d,
+            _dtype_code(q), _scale(scale, d), int(bool(causal)),
+            _stream(q.device)))

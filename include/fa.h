@@ -1,0 +1,177 @@
+/*
+ * fa.h — C ABI of the exact IO-aware attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Computes exact scaled-dot-product attention O = softmax(scale * Q K^T) V
+ * with tiled online softmax: the N x N score and probability matrices are
+ * never written to device memory; the backward recomputes them tile by tile
+ * from a saved per-row logsumexp.
+ *
+ * Pages cited (titles as published):
+ *   [TLDR]   "FlashAttention：メモリ効率的なアテンション計算" (tech-tldr.com)
+ *   [XYZ]    "FlashAttention: IOを意識した高速かつメモリ効率の高い厳密な
+ *            アテンション" (xyznot.com, summary of arXiv 2205.14135)
+ *   [REAPER] "3 · FlashAttention" (mkdocs.reaper.mx, chapter 3)
+ *   [LLMSYS] "출력을 누적해 메모리 이동을 줄이는 FlashAttention"
+ *            (llm-systems-engineering.pages.dev)
+ *   [Q67]    "FlashAttention：在线 softmax 与 IO-aware 注意力" (quant67.com)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Q, K, V, O, dO, dQ, dK, dV are dense row-major tensors of shape
+ *   B x H x N x d (d fastest, no padding): element (b, h, i, c) sits at
+ *   offset ((b*H + h)*N + i)*d + c.  LSE and the backward workspace rows are
+ *   B x H x N float32 arrays in the same (b, h, i) order.  Queries and keys
+ *   have the same length N.
+ * Pointers.  Every tensor pointer is a device pointer owned by the caller,
+ *   aligned to 16 bytes.  The library allocates no device memory and keeps no
+ *   mutable global state; concurrent calls on different streams are safe as
+ *   long as their output buffers do not overlap.
+ * Stream.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Work is enqueued and the call returns without synchronising;
+ *   outputs are valid once the stream has reached that point.
+ * Sizes.  B, H, N >= 0; when any of them is 0 the call does nothing and
+ *   returns FA_OK (pointers are not inspected).  d must be 64 or 128.
+ * dtype.  FA_BF16: Q, K, V, O, dO are bfloat16 (round-to-nearest-even
+ *   storage), arithmetic is bf16 x bf16 products accumulated in float32.
+ *   FA_F32: Q, K, V, O are float32 throughout (forward only).
+ *   LSE, dQ, dK, dV and the workspace are always float32.
+ * scale.  Finite and > 0 (the usual value is 1/sqrt(d), [Q67] section 1).
+ * Causal.  causal != 0 makes key j visible to query i iff j <= i.
+ * Errors.  Arguments are checked first, before any HIP call; a failed check
+ *   returns its FA_ERR_* code with nothing enqueued.  A failed kernel launch
+ *   returns FA_ERR_HIP.  Nothing is printed and nothing aborts.
+ */
+#ifndef EXACT_IO_AWARE_FA_H
+#define EXACT_IO_AWARE_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  FA_ERR_SHAPE = 2,       /* negative size, or sizes whose product overflows */
+  FA_ERR_DTYPE = 3,       /* dtype not FA_F32 / FA_BF16                     */
+  FA_ERR_UNSUPPORTED = 4, /* valid request this build does not provide      */
+  FA_ERR_MASK = 5,        /* block-mask geometry invalid                    */
+  FA_ERR_HIP = 6,         /* a HIP launch failed                            */
+  FA_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned        */
+  FA_ERR_ARG = 8,         /* scale not finite and > 0, workspace too small  */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * fa_fwd — forward pass.
+ *
+ * For each (b, h) and query row i:
+ *   S_ij = scale * q_i . k_j (masked entries -inf),
+ *   O_i  = sum_j softmax(S_i)_j v_j,
+ *   lse_i = ln sum_j exp(S_ij)   (natural log, scaled-score units).
+ * Defined by the three steps of standard attention ([Q67] section 1;
+ * [REAPER] section 3.1) and computed by the tiled online-softmax recurrence
+ * with an unnormalised accumulator divided once at the end ([TLDR] online
+ * softmax and tiling sections; [REAPER] sections 3.2-3.3; [LLMSYS] Fig. 2-3).
+ * A row that sees no key gets O_i = 0 and lse_i = -inf.
+ *
+ * q, k, v : inputs, B x H x N x d, dtype `dt`.
+ * o       : output, B x H x N x d, dtype `dt`.
+ * lse     : output, B x H x N float32.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
+                 float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                 fa_dtype dt, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_blocksparse — forward pass restricted to the nonzero blocks of a
+ * block mask ([XYZ] section "Block-Sparse FlashAttention").
+ *
+ * mask : device uint8 array, row-major, shape
+ *        ceil(N / block_m) x ceil(N / block_n), shared by every (b, h).
+ *        Key j is visible to query i iff mask[i / block_m][j / block_n] != 0
+ *        (AND the causal rule when causal != 0).  Tiles whose mask block is 0
+ *        are skipped entirely.  mask == NULL means every block is on (the
+ *        call is then identical to fa_fwd).
+ * block_m, block_n : positive multiples of 128.
+ * Other arguments and outputs as fa_fwd.  FA_ERR_MASK for invalid block
+ * sizes.
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, void* stream);
+
+/*
+ * fa_bwd — backward pass by recomputation ([TLDR] backward section; [XYZ]
+ * key ideas, recomputation; [REAPER] section 3.4; [Q67] section 5).
+ *
+ * Gradients of L = sum(O * dO) with respect to Q, K, V (exact gradient of
+ * fa_fwd; no gradient flows into lse).  With P the attention probabilities
+ * rebuilt from q, k and the saved lse:
+ *   D_i = sum_c dO_ic O_ic,  dV = P^T dO,  dP = dO V^T,
+ *   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Three kernels run in order on `stream`: a row pass computing D, a key-tile
+ * pass producing dK and dV, and a query-tile pass producing dQ.  No atomics;
+ * results are bitwise reproducible.
+ *
+ * q, k, v, o, dout : inputs, B x H x N x d, dtype `dt` (o and lse from
+ *                    fa_fwd on the same q, k, v, scale, causal).
+ * lse              : input, B x H x N float32.
+ * dq, dk, dv       : outputs, B x H x N x d float32 (overwritten).
+ * workspace        : caller-owned device scratch of at least
+ *                    fa_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *                    aligned; its contents on entry are ignored.
+ * FA_BF16 only; FA_F32 returns FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, float* dq, float* dk,
+                 float* dv, void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                 float scale, int causal, void* stream);
+
+/* Bytes of workspace fa_bwd needs (0 for empty problems). */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * The three passes of fa_bwd as separate calls, for callers that time or
+ * schedule them individually.  Calling preprocess, then dkdv and dq (in
+ * either order, after preprocess) on the same workspace equals fa_bwd.
+ *
+ * fa_bwd_preprocess : reads o, dout, lse; writes the per-row D and the
+ *                     base-2 logsumexp into `workspace`.
+ * fa_bwd_dkdv       : reads q, k, v, dout and `workspace`; writes dk, dv.
+ * fa_bwd_dq         : reads q, k, v, dout and `workspace`; writes dq.
+ * Arguments they do not use may be NULL.  Validation as fa_bwd.
+ */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d,
+                            fa_dtype dt, void* stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v,
+                      const void* dout, float* dk, float* dv,
+                      const void* workspace, size_t workspace_bytes,
+                      int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                      float scale, int causal, void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
+                    const void* dout, float* dq, const void* workspace,
+                    size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                    int64_t d, fa_dtype dt, float scale, int causal,
+                    void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Library version string, e.g. "exact_io_aware_amd 0.1.0 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_FA_H */

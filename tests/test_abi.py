@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects every invalid argument with the documented status before any HIP
+call (no GPU is touched; pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE = 0, 1, 2, 3
+FA_ERR_UNSUPPORTED, FA_ERR_MASK, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_ARG = (
+    4, 5, 6, 7, 8)
+F32, BF16 = 0, 1
+
+# Fake, aligned, never-dereferenced device addresses.
+P = 0x10000
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_io_aware_amd import _build, fa
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    return fa.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_fwd_blocksparse"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in fa.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.fa_version()
+    for code in range(9):
+        assert lib.fa_status_str(code).startswith(b"FA_")
+    assert lib.fa_status_str(99) == b"unknown fa_status"
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, dt=BF16,
+        scale=0.125, causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, B=-1) == FA_ERR_SHAPE
+    assert fwd(lib, N=-5) == FA_ERR_SHAPE
+    assert fwd(lib, dt=7) == FA_ERR_DTYPE
+    assert fwd(lib, d=32) == FA_ERR_UNSUPPORTED
+    assert fwd(lib, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd(lib, scale=float("nan")) == FA_ERR_ARG
+    assert fwd(lib, scale=float("inf")) == FA_ERR_ARG
+    assert fwd(lib, scale=0.0) == FA_ERR_ARG
+    assert fwd(lib, scale=-1.0) == FA_ERR_ARG
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: None}) == FA_ERR_NULL, name
+    for name in ("q", "k", "v", "o"):
+        assert fwd(lib, **{name: MISALIGNED}) == FA_ERR_ALIGN, name
+    assert fwd(lib, lse=P + 2) == FA_ERR_ALIGN
+    # sizes whose element count overflows
+    assert fwd(lib, B=1 << 40, H=1 << 20) == FA_ERR_SHAPE
+    assert fwd(lib, N=(1 << 30) + 1) == FA_ERR_SHAPE
+
+
+def test_empty_problems_are_noops(lib):
+    # Nothing to compute: FA_OK without looking at the (NULL) pointers.
+    for B, H, N in ((0, 4, 128), (2, 0, 128), (2, 4, 0)):
+        assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, B=B, H=H,
+                   N=N) == FA_OK
+        assert lib.fa_bwd(None, None, None, None, None, None, None, None,
+                          None, None, 0, B, H, N, 64, BF16, 0.125, 1,
+                          None) == FA_OK
+        assert lib.fa_bwd_workspace_bytes(B, H, N, 64) == 0
+
+
+def sparse(lib, mask=P, bm=128, bn=128, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=256, d=64, dt=BF16,
+             scale=0.125, causal=0)
+    a.update(kw)
+    return lib.fa_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                  a["B"], a["H"], a["N"], a["d"], a["dt"],
+                                  a["scale"], a["causal"], mask, bm, bn, None)
+
+
+def test_blocksparse_validation(lib):
+    assert sparse(lib, bm=64) == FA_ERR_MASK
+    assert sparse(lib, bn=100) == FA_ERR_MASK
+    assert sparse(lib, bm=0) == FA_ERR_MASK
+    assert sparse(lib, bn=-128) == FA_ERR_MASK
+    assert sparse(lib, d=48) == FA_ERR_UNSUPPORTED
+    assert sparse(lib, q=None) == FA_ERR_NULL
+    assert sparse(lib, N=0) == FA_OK
+
+
+def bwd(lib, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, B=2,
+             H=3, N=256, d=128, dt=BF16, scale=0.088, causal=1)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                      a["dq"], a["dk"], a["dv"], a["ws"], ws_bytes, a["B"],
+                      a["H"], a["N"], a["d"], a["dt"], a["scale"],
+                      a["causal"], None)
+
+
+def test_bwd_validation(lib):
+    need = lib.fa_bwd_workspace_bytes(2, 3, 256, 128)
+    assert need >= 2 * 2 * 3 * 256 * 4
+    assert bwd(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    assert bwd(lib, dt=9) == FA_ERR_DTYPE
+    assert bwd(lib, d=256) == FA_ERR_UNSUPPORTED
+    assert bwd(lib, ws_bytes=need - 4) == FA_ERR_ARG
+    assert bwd(lib, scale=float("nan")) == FA_ERR_ARG
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert bwd(lib, **{name: None}) == FA_ERR_NULL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv", "ws"):
+        assert bwd(lib, **{name: MISALIGNED}) == FA_ERR_ALIGN, name
+    assert bwd(lib, B=-2) == FA_ERR_SHAPE
+
+
+def test_bwd_pass_validation(lib):
+    ws = lib.fa_bwd_workspace_bytes(1, 1, 128, 64)
+    # preprocess needs o, dout, lse, workspace
+    assert lib.fa_bwd_preprocess(None, P, P, P, ws, 1, 1, 128, 64, BF16,
+                                 None) == FA_ERR_NULL
+    assert lib.fa_bwd_preprocess(P, P, P, P, ws - 1, 1, 1, 128, 64, BF16,
+                                 None) == FA_ERR_ARG
+    # dkdv needs q, k, v, dout, dk, dv; dq needs q, k, v, dout, dq
+    assert lib.fa_bwd_dkdv(P, P, P, P, None, P, P, ws, 1, 1, 128, 64, BF16,
+                           0.125, 0, None) == FA_ERR_NULL
+    assert lib.fa_bwd_dq(P, P, P, P, None, P, ws, 1, 1, 128, 64, BF16, 0.125,
+                         0, None) == FA_ERR_NULL
+    assert lib.fa_bwd_dq(P, P, P, P, P, P, ws, 1, 1, 128, 64, BF16, -0.1, 0,
+                         None) == FA_ERR_ARG
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1, 64) == 2 * 64 * 4
+    assert lib.fa_bwd_workspace_bytes(4, 16, 4096, 128) == 2 * 4 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 128, 32) == 0  # unsupported d
+    assert lib.fa_bwd_workspace_bytes(-1, 1, 128, 64) == 0
+
+
+def test_binding_fails_loudly_without_gpu_tensors(lib):
+    import torch
+
+    from exact_io_aware_amd import fa
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)  # CPU tensors are rejected, never computed on CPU

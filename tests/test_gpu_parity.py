@@ -1,0 +1,402 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the fp64 oracle.
+
+Bars: float32 path max-abs <= 1e-5; bfloat16 path max-abs <= 2e-2 and
+relative RMS <= 5e-3, with the oracle run on the bf16-rounded inputs.  At
+the full workload sizes the oracle computes sampled rows (forward) or whole
+sampled heads (backward); smaller cases are compared element by element.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_amd import fa, workloads
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-5
+BF16_MAX_ABS = 2e-2
+BF16_REL_RMS = 5e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.library()  # loud failure if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    sys.stdout.flush()
+    yield
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def compare(name, got, ref, fp32=False):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    ninf_g, ninf_r = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(ninf_g, ninf_r), f"{name}: -inf pattern differs"
+    ok = ~ninf_r
+    g, r = got[ok], ref[ok]
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    if g.size == 0:
+        return 0.0, 0.0
+    err = float(np.max(np.abs(g - r)))
+    rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+    if fp32:
+        assert err <= FP32_TOL, f"{name}: max-abs {err:.3e} > {FP32_TOL}"
+    else:
+        assert err <= BF16_MAX_ABS, f"{name}: max-abs {err:.3e}"
+        assert rel <= BF16_REL_RMS, f"{name}: rel-rms {rel:.3e}"
+    print(f"  {name}: max-abs {err:.3e} rel-rms {rel:.3e}", flush=True)
+    return err, rel
+
+
+def gen(B, H, N, d, seed, dtype="bf16", sigma=1.0, with_do=False, dev=None):
+    x = workloads.make_inputs(B, H, N, d, seed, sigma, dtype, with_do)
+    return {k: v.to(dev) for k, v in x.items()}
+
+
+# ---------------------------------------------------------------------------
+# float32 forward
+# ---------------------------------------------------------------------------
+
+def test_fp32_workload_1x1x256x64(dev):
+    w = workloads.workload("fp32_1x1x256x64")
+    x = gen(w["B"], w["H"], w["N"], w["d"], w["seed"], "f32", dev=dev)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"])
+    O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                w["scale"])
+    compare("O", f64(o), O, fp32=True)
+    compare("LSE", f64(lse), L, fp32=True)
+
+
+@pytest.mark.parametrize("N,d,causal", [(256, 128, True), (77, 64, False),
+                                        (200, 128, True), (1, 64, False),
+                                        (129, 64, True), (640, 64, True)])
+def test_fp32_shapes(dev, N, d, causal):
+    x = gen(2, 2, N, d, seed=100 + N, dtype="f32", dev=dev)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
+    O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale,
+                                causal)
+    compare("O", f64(o), O, fp32=True)
+    compare("LSE", f64(lse), L, fp32=True)
+
+
+def test_fp32_blocksparse_with_empty_row(dev):
+    N, d = 300, 64
+    x = gen(1, 2, N, d, seed=31, dtype="f32", dev=dev)
+    mask = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 0]], dtype=np.uint8)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"],
+                                       torch.from_numpy(mask).to(dev),
+                                       scale=0.125, causal=causal)
+        O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                    0.125, causal, mask, 128, 128)
+        compare("O", f64(o), O, fp32=True)
+        compare("LSE", f64(lse), L, fp32=True)
+        assert np.all(f64(o)[:, :, 128:256] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# bf16 forward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 64, 128, 200, 384, 1000])
+def test_bf16_fwd_shapes(dev, N, d, causal):
+    x = gen(2, 3, N, d, seed=200 + N + d, dev=dev)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
+    O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale,
+                                causal)
+    compare("O", f64(o), O)
+    compare("LSE", f64(lse), L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_workload_gpt2_8x16x1024x64(dev, causal):
+    w = workloads.workload("gpt2_8x16x1024x64")
+    x = gen(w["B"], w["H"], w["N"], w["d"], w["seed"], dev=dev)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"], causal=causal)
+    O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                w["scale"], causal)
+    compare("O", f64(o), O)
+    compare("LSE", f64(lse), L)
+
+
+def _sample_rows(N, seed, count=256):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 63, 64, 127, 128, 129, N // 2 - 1, N // 2, N - 129,
+             N - 128, N - 2, N - 1]
+    rows = set(int(r) for r in edges if 0 <= r < N)
+    rows.update(int(r) for r in rng.choice(N, size=min(count, N),
+                                           replace=False))
+    return np.array(sorted(rows))
+
+
+def test_bf16_workload_causal_2x32x8192x128(dev):
+    w = workloads.workload("causal_2x32x8192x128")
+    x = gen(w["B"], w["H"], w["N"], w["d"], w["seed"], sigma=w["sigma"],
+            dev=dev)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for (b, hh) in ((0, 0), (1, 31), (0, 17)):
+        rows = _sample_rows(w["N"], seed=b * 100 + hh)
+        q, k, v = (f64(x[n][b, hh]) for n in ("q", "k", "v"))
+        O, L = oracle.attention_fwd_head(q, k, v, w["scale"], True, rows=rows)
+        compare(f"O[{b},{hh}] sampled", f64(o[b, hh])[rows], O)
+        compare(f"LSE[{b},{hh}] sampled", f64(lse[b, hh])[rows], L)
+
+
+# ---------------------------------------------------------------------------
+# block-sparse forward
+# ---------------------------------------------------------------------------
+
+def test_bf16_workload_sparse_1x16x16384x64(dev):
+    w = workloads.workload("sparse_1x16x16384x64")
+    x = gen(w["B"], w["H"], w["N"], w["d"], w["seed"], dev=dev)
+    mask = workloads.workload_mask(w)
+    assert int(mask.sum()) == 4192
+    o, lse = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"],
+                                   torch.from_numpy(mask).to(dev),
+                                   scale=w["scale"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for hh in (0, 7, 15):
+        rows = _sample_rows(w["N"], seed=500 + hh, count=192)
+        q, k, v = (f64(x[n][0, hh]) for n in ("q", "k", "v"))
+        O, L = oracle.attention_fwd_head(q, k, v, w["scale"], False, mask,
+                                         128, 128, rows=rows)
+        compare(f"O[{hh}] sampled", f64(o[0, hh])[rows], O)
+        compare(f"LSE[{hh}] sampled", f64(lse[0, hh])[rows], L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_special_masks(dev, d):
+    N = 640
+    x = gen(1, 4, N, d, seed=41, dev=dev)
+    T = 5
+    scale = 1 / math.sqrt(d)
+    dense_o, dense_l = fa.fa_fwd(x["q"], x["k"], x["v"], scale=scale)
+    ones = torch.ones(T, T, dtype=torch.uint8, device=dev)
+    o1, l1 = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], ones, scale=scale)
+    assert torch.equal(o1, dense_o) and torch.equal(l1, dense_l), \
+        "all-ones mask must equal the dense kernel bitwise"
+    o_none, l_none = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], None,
+                                           scale=scale)
+    assert torch.equal(o_none, dense_o) and torch.equal(l_none, dense_l)
+    # diagonal-only mask == dense attention on each 128-token chunk
+    diag = torch.eye(T, dtype=torch.uint8, device=dev)
+    od, ld = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], diag, scale=scale)
+    chunk = lambda t: t.reshape(1 * 4 * T, 1, 128, d).contiguous()  # noqa
+    oc, lc = fa.fa_fwd(chunk(x["q"]), chunk(x["k"]), chunk(x["v"]),
+                       scale=scale)
+    assert torch.equal(od.reshape(oc.shape), oc)
+    assert torch.equal(ld.reshape(lc.shape), lc)
+    # random mask with an empty block row, causal and not, and 256-row blocks
+    rng = np.random.default_rng(3)
+    m = (rng.random((T, T)) < 0.5).astype(np.uint8)
+    m[2] = 0
+    for causal in (False, True):
+        o, lse = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"],
+                                       torch.from_numpy(m).to(dev),
+                                       scale=scale, causal=causal)
+        O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                    scale, causal, m, 128, 128)
+        compare(f"O causal={causal}", f64(o), O)
+        compare(f"LSE causal={causal}", f64(lse), L)
+    m2 = np.array([[1, 0, 1, 1, 0], [0, 1, 1, 0, 1], [1, 1, 0, 0, 1]],
+                  dtype=np.uint8)
+    o, lse = fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"],
+                                   torch.from_numpy(m2).to(dev), block_m=256,
+                                   block_n=128, scale=scale, causal=True)
+    O, L = oracle.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale,
+                                True, m2, 256, 128)
+    compare("O 256x128 blocks", f64(o), O)
+    compare("LSE 256x128 blocks", f64(lse), L)
+
+
+# ---------------------------------------------------------------------------
+# bf16 backward
+# ---------------------------------------------------------------------------
+
+def _bwd_case(dev, B, H, N, d, seed, causal, sigma=1.0, heads=None):
+    x = gen(B, H, N, d, seed, sigma=sigma, with_do=True, dev=dev)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse,
+                           scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    got = {n: np.stack([f64(t[b, h]) for b, h in heads])
+           for n, t in (("dQ", dq), ("dK", dk), ("dV", dv))}
+    ref = {n: [] for n in got}
+    for b, h in heads:
+        r = oracle.attention_bwd_head(*(f64(x[n][b, h]) for n in
+                                        ("q", "k", "v", "do")), scale, causal)
+        for n, val in zip(("dQ", "dK", "dV"), r):
+            ref[n].append(val)
+    for n in got:
+        compare(n, got[n], np.stack(ref[n]))
+    return x, (o, lse), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 100, 128, 300, 513])
+def test_bf16_bwd_shapes(dev, N, d, causal):
+    _bwd_case(dev, 1, 2, N, d, seed=300 + N + d, causal=causal)
+
+
+def test_bf16_bwd_single_key_closed_form(dev):
+    # N = 1: dQ = dK = 0 and dV = dO.
+    x, _, (dq, dk, dv) = _bwd_case(dev, 2, 2, 1, 64, seed=9, causal=True)
+    assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
+    compare("dV vs dO", f64(dv), f64(x["do"]))
+
+
+def test_bf16_workload_bwd_4x16x4096x128(dev):
+    w = workloads.workload("bwd_4x16x4096x128")
+    _bwd_case(dev, w["B"], w["H"], w["N"], w["d"], w["seed"], True,
+              heads=[(0, 0), (2, 7), (3, 15)])
+
+
+def test_bf16_bwd_metric_shape_2x32x8192x128(dev):
+    w = workloads.workload("causal_2x32x8192x128")
+    _bwd_case(dev, w["B"], w["H"], w["N"], w["d"], w["seed"], True,
+              sigma=w["sigma"], heads=[(0, 3), (1, 30)])
+
+
+def test_bwd_passes_equal_fused_call(dev):
+    B, H, N, d = 1, 2, 320, 128
+    x = gen(B, H, N, d, seed=61, with_do=True, dev=dev)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], causal=True)
+    dq, dk, dv = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse,
+                           causal=True)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device=dev)
+    dq2, dk2, dv2 = (torch.empty_like(t) for t in (dq, dk, dv))
+    fa.fa_bwd_preprocess(o, x["do"], lse, ws)
+    fa.fa_bwd_dq(x["q"], x["k"], x["v"], x["do"], ws, dq2, causal=True)
+    fa.fa_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], ws, dk2, dv2, causal=True)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+# ---------------------------------------------------------------------------
+# worked examples, closed forms, determinism, streams
+# ---------------------------------------------------------------------------
+
+def _embed(Qs, Ks, Vs, dtype, dev, d=64, N=128):
+    """Place a small example (coordinates in dims 0-1) in a d=64, N=128
+    problem: tested queries get dim 63 = 1, real keys dim 63 = 0, padding
+    keys dim 63 = -1e4 (score about -1e4, weight exactly 0)."""
+    q = torch.zeros(1, 1, N, d, dtype=torch.float64)
+    k = torch.zeros(1, 1, N, d, dtype=torch.float64)
+    v = torch.zeros(1, 1, N, d, dtype=torch.float64)
+    Qs, Ks, Vs = (torch.tensor(a, dtype=torch.float64) for a in (Qs, Ks, Vs))
+    q[0, 0, :Qs.shape[0], :Qs.shape[1]] = Qs
+    q[0, 0, :Qs.shape[0], 63] = 1.0
+    k[0, 0, :Ks.shape[0], :Ks.shape[1]] = Ks
+    k[0, 0, Ks.shape[0]:, 63] = -1e4
+    v[0, 0, :Vs.shape[0], :Vs.shape[1]] = Vs
+    t = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return q.to(t).to(dev), k.to(t).to(dev), v.to(t).to(dev)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_worked_examples_embedded(dev, dtype):
+    from tests.oracle_pins import _golden
+    g = _golden()
+    tol = 5e-4 + (1e-9 if dtype == "f32" else 4e-3)  # printed 3 decimals
+    f2 = g["fig2_streamed_pairs"]
+    q, k, v = _embed([[1.0]], [[s] for s in f2["scores"]], f2["values"], dtype,
+                     dev)
+    o, lse = fa.fa_fwd(q, k, v, scale=1.0)
+    O, L = oracle.attention_fwd(f64(q), f64(k), f64(v), 1.0)
+    compare("fig2 O", f64(o), O, fp32=(dtype == "f32"))
+    compare("fig2 LSE", f64(lse), L, fp32=(dtype == "f32"))
+    assert np.max(np.abs(f64(o)[0, 0, 0, :2] - f2["output"])) <= tol
+    f3 = g["fig3_two_query_tile"]
+    q, k, v = _embed(f3["Q"], f3["K"], f3["V"], dtype, dev)
+    o, lse = fa.fa_fwd(q, k, v, scale=1.0)
+    O, L = oracle.attention_fwd(f64(q), f64(k), f64(v), 1.0)
+    compare("fig3 O", f64(o), O, fp32=(dtype == "f32"))
+    assert np.max(np.abs(f64(o)[0, 0, :2, :2] - np.array(f3["output"]))) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_equal_scores_and_unit_values(dev, dtype):
+    N, d = 300, 64
+    x = gen(1, 2, N, d, seed=71, dtype=dtype, dev=dev)
+    zq = torch.zeros_like(x["q"])
+    fp32 = dtype == "f32"
+    for causal in (False, True):
+        o, lse = fa.fa_fwd(zq, x["k"], x["v"], causal=causal)
+        v = f64(x["v"])
+        if causal:
+            ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[:, None]
+            lref = np.broadcast_to(np.log(np.arange(1, N + 1)), (1, 2, N))
+        else:
+            ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+            lref = np.full((1, 2, N), math.log(N))
+        compare("equal-score O", f64(o), ref, fp32=fp32)
+        compare("equal-score LSE", f64(lse), lref, fp32=fp32)
+        ones = torch.ones_like(x["v"])
+        o, _ = fa.fa_fwd(x["q"], x["k"], ones, causal=causal)
+        compare("V=1 O", f64(o), np.ones(o.shape), fp32=fp32)
+
+
+def test_large_score_shift(dev):
+    # Adding c to every score of a row leaves O unchanged and adds c to LSE;
+    # c = 1000 exercises the max subtraction (exp(1000) overflows fp32).
+    N, d = 256, 128
+    x = gen(1, 2, N, d, seed=81, dev=dev)
+    scale = 1 / math.sqrt(d)
+    q, k = x["q"].clone(), x["k"].clone()
+    k[..., 127] = 1.0
+    q[..., 127] = 0.0
+    o0, l0 = fa.fa_fwd(q, k, x["v"], scale=scale, causal=True)
+    q[..., 127] = 1000.0 / scale
+    o1, l1 = fa.fa_fwd(q, k, x["v"], scale=scale, causal=True)
+    O, L = oracle.attention_fwd(f64(q), f64(k), f64(x["v"]), scale, True)
+    compare("shifted O", f64(o1), O)
+    compare("shifted LSE", f64(l1), L)
+    compare("shift leaves O", f64(o1), f64(o0))
+
+
+def test_determinism(dev):
+    B, H, N, d = 2, 4, 1000, 128
+    x = gen(B, H, N, d, seed=91, with_do=True, dev=dev)
+    r1 = fa.fa_fwd(x["q"], x["k"], x["v"], causal=True)
+    g1 = fa.fa_bwd(x["q"], x["k"], x["v"], *r1[:1], x["do"], r1[1], causal=True)
+    r2 = fa.fa_fwd(x["q"], x["k"], x["v"], causal=True)
+    g2 = fa.fa_bwd(x["q"], x["k"], x["v"], *r2[:1], x["do"], r2[1], causal=True)
+    for a, b in zip(r1 + g1, r2 + g2):
+        assert torch.equal(a, b), "results must be bitwise reproducible"
+
+
+def test_side_stream(dev):
+    x = gen(1, 2, 256, 64, seed=92, dev=dev)
+    ref_o, ref_l = fa.fa_fwd(x["q"], x["k"], x["v"])
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        o, lse = fa.fa_fwd(x["q"], x["k"], x["v"])
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
