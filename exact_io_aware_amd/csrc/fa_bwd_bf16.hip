@@ -23,13 +23,15 @@
 //                and dV^T in registers; each is written once.
 //   dq         : a workgroup owns 128 queries (32 per wave, Q and dO held in
 //                registers) and sweeps the key tiles, accumulating dQ^T.
-// All four contractions per tile pair run on v_mfma_f32_32x32x16_bf16.  The
-// dkdv pass computes S = Q K^T so that each lane owns one key (the N index
-// of the D layout); P and dS then already have the B-operand layout for the
-// contractions over queries, and only Q and dO need a transposed copy in
-// LDS.  The dq pass computes S^T = K Q^T (lane = query) for the same reason
-// and needs a transposed copy of K.  Causal key/query tiles that are fully
-// masked are skipped ([REAPER], causal-mask question).
+// All contractions run on v_mfma_f32_32x32x16_bf16.  The dkdv pass computes
+// S = Q K^T so that each lane owns one key (the N index of the D layout); P
+// and dS then already have the B-operand layout for the contractions over
+// queries.  The dq pass computes S^T = K Q^T (lane = query) for the same
+// reason.  Every LDS tile is stored once, row-major; the transposed operands
+// (Q^T and dO^T in dkdv, K^T in dq) come from ds_read_b64_tr_b16 reads of
+// those same tiles, with one XOR swizzle that is conflict-free for both the
+// row-wise and the transposed read pattern.  Causal key/query tiles that are
+// fully masked are skipped ([REAPER], causal-mask question).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -86,18 +88,36 @@ struct KVTile {
   static constexpr int KS = D / 16;
   static constexpr int QB = BRQ / 32;
   static constexpr int DB = D / 32;
-  static constexpr int ROW = D * 2;                   // row-major row bytes
-  static constexpr int TROW = BRQ * 2;                // transposed row bytes
-  static constexpr int T_BYTES = BRQ * ROW;           // == D * TROW
-  // stage layout: Q | Q^T | dO | dO^T | lse2[BRQ] | D[BRQ]
-  static constexpr int OFF_QT = T_BYTES;
-  static constexpr int OFF_DO = 2 * T_BYTES;
-  static constexpr int OFF_DOT = 3 * T_BYTES;
-  static constexpr int OFF_L = 4 * T_BYTES;
+  static constexpr int CPR = D / 8;
+  static constexpr int ROW = D * 2;
+  static constexpr int T_BYTES = BRQ * ROW;
+  // stage layout: Q | dO | lse2[BRQ] | D[BRQ]
+  static constexpr int OFF_DO = T_BYTES;
+  static constexpr int OFF_L = 2 * T_BYTES;
   static constexpr int OFF_D = OFF_L + BRQ * 4;
   static constexpr int STAGE = OFF_D + BRQ * 4;
-  static_assert((BRQ / 4) * (D / 8) == 256, "one 4x8 unit per thread");
+  static constexpr int LPT = BRQ * CPR / 256;
+  static_assert(LPT == 4, "four 16-B chunks of Q and of dO per thread");
 };
+
+// Per-lane offsets of the transposed operand of a 16-row k-step: source lane
+// s = lane % 16 of group g = lane / 16 addresses row r2*8 + h*4 + s/4 at
+// column db*32 + 16*(g & 1) + 4*(s % 4) (r2 = 0: slots 0-3, r2 = 1: slots
+// 4-7).  The resulting slot order matches the register order of an MFMA
+// D-layout block (rows {h*4 + 0..3} then {8 + h*4 + 0..3}).
+template <int D, int DB>
+__device__ __forceinline__ void tr_offsets(int lane, int toff[DB][2]) {
+  const int s16 = lane & 15, g = lane >> 4, h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int col = db * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+      toff[db][r2] = tile_off<D>(r2 * 8 + h * 4 + (s16 >> 2), col >> 3) +
+                     (col & 7) * 2;
+    }
+  }
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -124,7 +144,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + l32;
 
-  // K and V as B operands (lane = key, slots = 8 consecutive d).
+  // K and V as B operands (lane = key, slots = 8 consecutive d).  Keys past
+  // the end read a valid row; their dK, dV are never stored.
   bf16x8 kf[T::KS], vf[T::KS];
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) {
@@ -138,19 +159,26 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     adv[db] = zero16();
   }
 
+  int aoff[T::KS];  // row-wise A operand: row l32 (+ qb*32), chunk ks*2 + h
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) aoff[ks] = tile_off<D>(l32, ks * 2 + h);
+  int toff[T::DB][2];
+  tr_offsets<D, T::DB>(lane, toff);
+
   const int n_qt = (n + T::BRQ - 1) / T::BRQ;
   const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
 
-  const int dg = tid % (D / 8);
-  const int qg = tid / (D / 8);
-  u32x4 qpre[4], dopre[4];
+  // Rows past the end read row n - 1; their lse2 = +inf makes every
+  // rebuilt probability of those rows exactly 0, so they add nothing.
+  u32x4 qpre[T::LPT], dopre[T::LPT];
   float lpre = 0.f, dpre = 0.f;
   auto load_tile = [&](int qt) {
     const int qb0 = qt * T::BRQ;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      qpre[r] = load_row16(Q + hoff, qb0 + qg * 4 + r, n, D, dg * 8);
-      dopre[r] = load_row16(dO + hoff, qb0 + qg * 4 + r, n, D, dg * 8);
+    for (int i = 0; i < T::LPT; ++i) {
+      const int e = tid + 256 * i;
+      qpre[i] = load_row16(Q + hoff, qb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
+      dopre[i] = load_row16(dO + hoff, qb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
     }
     if (tid < T::BRQ) {
       const int row = qb0 + tid;
@@ -161,26 +189,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   auto store_tile = [&](int stage) {
     unsigned char* st = smem + stage * T::STAGE;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<u32x4*>(st + lds_off<T::ROW>(qg * 4 + r, dg)) = qpre[r];
-      *reinterpret_cast<u32x4*>(st + T::OFF_DO + lds_off<T::ROW>(qg * 4 + r, dg)) =
-          dopre[r];
-    }
-    const int pos = (qg >> 2) * 16 + perm_run(qg & 3) * 4;
-    u32x2 tr[8];
-    transpose4x8(qpre, tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<u32x2*>(st + T::OFF_QT +
-                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
-                                (pos & 7) * 2) = tr[e];
-    }
-    transpose4x8(dopre, tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<u32x2*>(st + T::OFF_DOT +
-                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
-                                (pos & 7) * 2) = tr[e];
+    for (int i = 0; i < T::LPT; ++i) {
+      const int e = tid + 256 * i;
+      const int off = tile_off<D>(e / T::CPR, e % T::CPR);
+      *reinterpret_cast<u32x4*>(st + off) = qpre[i];
+      *reinterpret_cast<u32x4*>(st + T::OFF_DO + off) = dopre[i];
     }
     if (tid < T::BRQ) {
       reinterpret_cast<float*>(st + T::OFF_L)[tid] = lpre;
@@ -205,11 +218,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
-        const int off = lds_off<T::ROW>(qb * 32 + l32, ks * 2 + h);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(st + off);
-        const bf16x8 ado = *reinterpret_cast<const bf16x8*>(st + T::OFF_DO + off);
-        s = mfma32(aq, kf[ks], s);
-        dp = mfma32(ado, vf[ks], dp);
+        const unsigned char* pa = st + qb * 32 * T::ROW + aoff[ks];
+        s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kf[ks], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_DO), vf[ks], dp);
       }
       // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.
       const bool need_mask = CAUSAL && qq0 < kw0 + 31;
@@ -226,17 +237,22 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           dp[i] = p * (dp[i] - Dv[t]);
         }
       }
-      const bf16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 1);
-      const bf16x8 sf0 = pack8(dp, 0), sf1 = pack8(dp, 1);
-      // dV^T += dO^T P and dK^T += Q^T dS (M = d, N = key, K = query).
+      const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
+      const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
+      // dV^T += dO^T P and dK^T += Q^T dS (M = d, N = key, K = query); the
+      // transposed operands come from transpose reads of the Q / dO tiles.
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int o0 = lds_off<T::TROW>(db * 32 + l32, (qb * 2) * 2 + h);
-        const int o1 = lds_off<T::TROW>(db * 32 + l32, (qb * 2 + 1) * 2 + h);
-        adv[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_DOT + o0), pf0, adv[db]);
-        adv[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_DOT + o1), pf1, adv[db]);
-        adk[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_QT + o0), sf0, adk[db]);
-        adk[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_QT + o1), sf1, adk[db]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const unsigned char* pk = st + (qb * 2 + s2) * 16 * T::ROW;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const bf16x8 a_do = join_tr16(lds_read_tr16(pk + T::OFF_DO + toff[db][0]),
+                                        lds_read_tr16(pk + T::OFF_DO + toff[db][1]));
+          const bf16x8 a_q = join_tr16(lds_read_tr16(pk + toff[db][0]),
+                                       lds_read_tr16(pk + toff[db][1]));
+          adv[db] = mfma32(a_do, pf[s2], adv[db]);
+          adk[db] = mfma32(a_q, sf[s2], adk[db]);
+        }
       }
     }
     stage ^= 1;
@@ -273,18 +289,18 @@ struct QTile {
   static constexpr int KS = D / 16;
   static constexpr int KB = BCK / 32;
   static constexpr int DB = D / 32;
+  static constexpr int CPR = D / 8;
   static constexpr int ROW = D * 2;
-  static constexpr int TROW = BCK * 2;
   static constexpr int T_BYTES = BCK * ROW;
-  // stage layout: K | K^T | V
-  static constexpr int OFF_KT = T_BYTES;
-  static constexpr int OFF_V = 2 * T_BYTES;
-  static constexpr int STAGE = 3 * T_BYTES;
-  static_assert((BCK / 4) * (D / 8) == 256, "one 4x8 unit per thread");
+  // stage layout: K | V
+  static constexpr int OFF_V = T_BYTES;
+  static constexpr int STAGE = 2 * T_BYTES;
+  static constexpr int LPT = BCK * CPR / 256;
+  static_assert(LPT == 4, "four 16-B chunks of K and of V per thread");
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ ws_d,
@@ -320,37 +336,34 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) adq[db] = zero16();
 
+  int aoff[T::KS];  // row-wise A operand: row l32 (+ kb*32), chunk ks*2 + h
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) aoff[ks] = tile_off<D>(l32, ks * 2 + h);
+  int toff[T::DB][2];
+  tr_offsets<D, T::DB>(lane, toff);
+
   const int n_kt = (n + T::BCK - 1) / T::BCK;
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(n_kt, (min(q0 + T::BRQ, n) - 1) / T::BCK + 1);
 
-  const int dg = tid % (D / 8);
-  const int kg = tid / (D / 8);
-  u32x4 kpre[4], vpre[4];
+  u32x4 kpre[T::LPT], vpre[T::LPT];
   auto load_tile = [&](int kt) {
     const int kb0 = kt * T::BCK;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      kpre[r] = load_row16(K + hoff, kb0 + kg * 4 + r, n, D, dg * 8);
-      vpre[r] = load_row16(V + hoff, kb0 + kg * 4 + r, n, D, dg * 8);
+    for (int i = 0; i < T::LPT; ++i) {
+      const int e = tid + 256 * i;
+      kpre[i] = load_row16(K + hoff, kb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
+      vpre[i] = load_row16(V + hoff, kb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
     }
   };
   auto store_tile = [&](int stage) {
     unsigned char* st = smem + stage * T::STAGE;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<u32x4*>(st + lds_off<T::ROW>(kg * 4 + r, dg)) = kpre[r];
-      *reinterpret_cast<u32x4*>(st + T::OFF_V + lds_off<T::ROW>(kg * 4 + r, dg)) =
-          vpre[r];
-    }
-    const int pos = (kg >> 2) * 16 + perm_run(kg & 3) * 4;
-    u32x2 tr[8];
-    transpose4x8(kpre, tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<u32x2*>(st + T::OFF_KT +
-                                lds_off<T::TROW>(dg * 8 + e, pos >> 3) +
-                                (pos & 7) * 2) = tr[e];
+    for (int i = 0; i < T::LPT; ++i) {
+      const int e = tid + 256 * i;
+      const int off = tile_off<D>(e / T::CPR, e % T::CPR);
+      *reinterpret_cast<u32x4*>(st + off) = kpre[i];
+      *reinterpret_cast<u32x4*>(st + T::OFF_V + off) = vpre[i];
     }
   };
 
@@ -363,33 +376,40 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const unsigned char* st = smem + stage * T::STAGE;
     const int kbase = kt * T::BCK;
     if (!CAUSAL || kbase <= qw0 + 31) {
-      const bool need_mask = CAUSAL && kbase + T::BCK - 1 > qw0;
+      // Keys past the end read a valid row and must be masked explicitly.
+      const bool need_mask =
+          (CAUSAL && kbase + T::BCK - 1 > qw0) || (kbase + T::BCK > n);
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
         // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
-          const int off = lds_off<T::ROW>(kb * 32 + l32, ks * 2 + h);
-          s = mfma32(*reinterpret_cast<const bf16x8*>(st + off), qf[ks], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_V + off),
-                      dof[ks], dp);
+          const unsigned char* pa = st + kb * 32 * T::ROW + aoff[ks];
+          s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
+          dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
-          const int kj = kbase + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-          if (need_mask && kj > qrow) p = 0.f;
+          if (need_mask) {
+            const int kj = kbase + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+            if ((CAUSAL && kj > qrow) || kj >= n) p = 0.f;
+          }
           dp[i] = p * (dp[i] - drow);
         }
-        const bf16x8 sf0 = pack8(dp, 0), sf1 = pack8(dp, 1);
-        // dQ^T += K^T dS^T (M = d, N = query, K = key).
+        const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
+        // dQ^T += K^T dS^T (M = d, N = query, K = key); K^T from transpose
+        // reads of the K tile.
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-          const int o0 = lds_off<T::TROW>(db * 32 + l32, (kb * 2) * 2 + h);
-          const int o1 = lds_off<T::TROW>(db * 32 + l32, (kb * 2 + 1) * 2 + h);
-          adq[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_KT + o0), sf0, adq[db]);
-          adq[db] = mfma32(*reinterpret_cast<const bf16x8*>(st + T::OFF_KT + o1), sf1, adq[db]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const unsigned char* pk = st + (kb * 2 + s2) * 16 * T::ROW;
+#pragma unroll
+          for (int db = 0; db < T::DB; ++db) {
+            const bf16x8 a = join_tr16(lds_read_tr16(pk + toff[db][0]),
+                                       lds_read_tr16(pk + toff[db][1]));
+            adq[db] = mfma32(a, sf[s2], adq[db]);
+          }
         }
       }
     }

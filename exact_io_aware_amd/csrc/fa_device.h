@@ -70,58 +70,59 @@ __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
 }
 
-// ---------------------------------------------------------------------------
-// Swizzled LDS tiles.  A tile is a stack of rows of ROW_BYTES bytes, each
-// split into 16-byte chunks.  Chunk c of row r is stored at chunk slot
-// c ^ swz(r), so that the 16 rows read together by one quarter-wave's
-// 16-byte loads (same logical chunk, consecutive rows) land on distinct
-// banks.
-// ---------------------------------------------------------------------------
-template <int ROW_BYTES>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(ROW_BYTES == 128 || ROW_BYTES == 256, "row size");
-  if constexpr (ROW_BYTES == 256) {
-    return r & 15;
+// Chunk swizzle for a row-major bf16 tile with D columns that is read both
+// row-wise (16 consecutive rows, one 16-B chunk each, as an MFMA A operand)
+// and by transpose reads (8 consecutive rows, one 64-B run each).  The
+// row-wise pattern needs the swizzle to be a bijection over 16 consecutive
+// rows; the transpose pattern needs rows 0-3 of each group of 8 to land on
+// disjoint 64-B bank groups.  A bit rotation of the row index gives both:
+//   D = 128 (256-B rows): bits (r1 r0 | r3 r2) of r;
+//   D = 64 (128-B rows, two rows per bank line): t = (r >> 1) & 7 rotated.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
   } else {
-    return (r >> 1) & 7;
+    const int t = (r >> 1) & 7;
+    return ((t & 1) << 2) | (t >> 1);
   }
 }
 
-template <int ROW_BYTES>
-__device__ __forceinline__ int lds_off(int r, int c) {
-  return r * ROW_BYTES + ((c ^ swz<ROW_BYTES>(r)) << 4);
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * (D * 2) + ((c ^ tile_swz<D>(r)) << 4);
 }
 
-// Position of key offset o (0..15) inside a 16-key group of a transposed
-// tile.  The D layout of an MFMA result gives half h of the wave the keys
-// {h*4 + 0..3, 8 + h*4 + 0..3} of each 16-key group, while an operand slot
-// j of half h reads position h*8 + j; storing runs of 4 keys in the order
-// 0, 2, 1, 3 makes the two agree.  (The contraction index is a dummy, so any
-// order works as long as both operands use the same one.)
-__device__ __forceinline__ int perm_run(int run) {
-  return ((run & 1) << 1) | (run >> 1);  // 0->0, 1->2, 2->1, 3->3
+// ---------------------------------------------------------------------------
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte rows addressed by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.  If source lane s
+// addresses row R(s / 4) at column C + 4 * (s % 4) of a row-major bf16 tile,
+// lane i therefore receives column C + i of rows R(0..3): four consecutive
+// contraction-index values at a fixed output column, which is the MFMA
+// operand layout of the transposed tile.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// Transpose 4 rows x 8 columns of bf16 (in[r] = 16 bytes of row r) into
-// 8 columns x 4 rows: out[e] = {row0, row1, row2, row3} of column e packed in
-// two dwords.
-__device__ __forceinline__ void transpose4x8(const u32x4 in[4], u32x2 out[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    out[e][0] = __builtin_amdgcn_perm(in[1][e >> 1], in[0][e >> 1], sel);
-    out[e][1] = __builtin_amdgcn_perm(in[3][e >> 1], in[2][e >> 1], sel);
-  }
+// Two transpose reads (slots 0-3 and 4-7) joined into one MFMA operand.
+__device__ __forceinline__ bf16x8 join_tr16(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// 16-byte global load of row `row` (zero when row >= n).
+// 16-byte global load of row `row`, clamped to the last row n - 1 (n >= 1).
+// Rows past the end therefore read valid memory with arbitrary finite
+// contents; every caller masks or discards what they contribute.
 __device__ __forceinline__ u32x4 load_row16(const bf16* base, int row, int n,
                                             int ld, int col) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  if (row < n) {
-    z = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + col);
-  }
-  return z;
+  const int r = min(row, n - 1);
+  return *reinterpret_cast<const u32x4*>(base + (int64_t)r * ld + col);
 }
 
 // ---------------------------------------------------------------------------
@@ -131,6 +132,12 @@ __device__ __forceinline__ u32x4 load_row16(const bf16* base, int row, int n,
 // the K/V re-reads of that head hit the same L2.
 // ---------------------------------------------------------------------------
 constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ int xcd_logical_id(int g, int total) {
+  if (total % kNumXcd != 0) return g;
+  const int per = total / kNumXcd;
+  return (g % kNumXcd) * per + g / kNumXcd;
+}
 
 // ---------------------------------------------------------------------------
 // Host-side launch returning the launch's own status (hipLaunchKernel does
@@ -147,12 +154,6 @@ inline hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block,
                                 typename ident<P>::type... args) {
   void* argv[] = {(void*)&args..., nullptr};
   return hipLaunchKernel((const void*)kern, grid, block, argv, 0, s);
-}
-
-__device__ __forceinline__ int xcd_logical_id(int g, int total) {
-  if (total % kNumXcd != 0) return g;
-  const int per = total / kNumXcd;
-  return (g % kNumXcd) * per + g / kNumXcd;
 }
 
 }  // namespace fa

@@ -27,11 +27,15 @@
 //     two halves of the wave, and the rescale factor is a per-lane scalar.
 //   * The exponentials are exp2 with scale*log2(e) folded into one FMA.
 //   * O^T = V^T P^T on the same MFMA: P leaves the exponentials already in
-//     the B-operand layout (after bf16 rounding), and V^T is stored in LDS
-//     with its keys in the matching permuted order, so P never touches LDS.
+//     the B-operand layout (after bf16 rounding).  V stays row-major in LDS
+//     and its transposed A operand is read with ds_read_b64_tr_b16; the key
+//     order of those reads matches the key order of P's registers (the
+//     contraction index is a dummy, so both sides only have to agree).
 //   * K and V tiles are double-buffered in LDS (one barrier per tile); the
 //     next tile's global loads are issued before the current tile's math.
-//   * LDS rows are XOR-swizzled in 16-byte chunks against bank conflicts.
+//   * 16-byte chunks are XOR-swizzled per row so that both the row-wise
+//     stores and the fragment reads are free of bank conflicts; every LDS
+//     read address is a loop-invariant per-lane base plus a constant.
 //   * The workgroup order keeps each head on one XCD (shared L2) and, under
 //     the causal rule, starts the longest query tiles first.
 #include "fa_device.h"
@@ -49,15 +53,29 @@ struct FwdTile {
   static constexpr int KB = BC / 32;                  // 32-key blocks per tile
   static constexpr int KK = BC / 16;                  // 16-key k-steps of PV
   static constexpr int DB = D / 32;                   // 32-wide blocks of d
-  static constexpr int CPR = D / 8;                   // 16-B chunks per K row
-  static constexpr int KROW = D * 2;                  // bytes per K row
-  static constexpr int VROW = BC * 2;                 // bytes per V^T row
-  static constexpr int K_BYTES = BC * KROW;
-  static constexpr int V_BYTES = D * VROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static_assert((BC / 4) * (D / 8) == 256, "one V unit per thread");
-  static_assert(BC * D / 8 == 4 * 256, "four K chunks per thread");
+  static constexpr int CPR = D / 8;                   // 16-B chunks per row
+  static constexpr int ROW = D * 2;                   // bytes per K / V row
+  static constexpr int K_BYTES = BC * ROW;
+  static constexpr int STAGE = 2 * K_BYTES;           // K tile then V tile
+  static constexpr int LPT = BC * CPR / 256;          // chunks per thread
+  static_assert(LPT == 4, "four 16-B chunks of K and of V per thread");
 };
+
+// Chunk swizzle of the K tile.  Fragment reads take one chunk from 16
+// consecutive rows per quarter-wave: with 256-B rows XOR by (row & 15), with
+// 128-B rows (two rows per bank line) XOR by ((row >> 1) & 7).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return (D == 128) ? (row & 15) : ((row >> 1) & 7);
+}
+// Chunk swizzle of the V tile.  A transpose read takes a 64-B run (4 chunks)
+// from 8 consecutive rows; XOR-ing bits 2-3 of the chunk index by
+// (row & 3) (256-B rows) or by ((row >> 1) & 1) (128-B rows) puts rows 0-3
+// on disjoint banks, so each read costs the minimum two LDS cycles.
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return (D == 128) ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -115,42 +133,56 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     return kt;
   };
 
-  // Global -> register staging of one K/V tile.  K: 4 chunks of 16 B per
-  // thread in row-major order.  V: thread owns 4 consecutive keys x 8
-  // consecutive d (dg = d group, kg = key group).
-  const int dg = tid % (D / 8);
-  const int kg = tid / (D / 8);
-  u32x4 kpre[4], vpre[4];
+  // Global -> register staging of one K/V tile: thread tid owns chunks
+  // e = tid + 256 i (row e / CPR, chunk e % CPR) of both tiles, so each
+  // quarter-wave stores whole rows (conflict-free under the row swizzles).
+  u32x4 kpre[T::LPT], vpre[T::LPT];
   auto load_tile = [&](int kt) {
     const int kbase = kt * T::BC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < T::LPT; ++i) {
       const int e = tid + 256 * i;
       kpre[i] = load_row16(Kh, kbase + e / T::CPR, n, D, (e % T::CPR) * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      vpre[r] = load_row16(Vh, kbase + kg * 4 + r, n, D, dg * 8);
+      vpre[i] = load_row16(Vh, kbase + e / T::CPR, n, D, (e % T::CPR) * 8);
     }
   };
   auto store_tile = [&](int stage) {
     unsigned char* sk = smem + stage * T::STAGE;
     unsigned char* sv = sk + T::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < T::LPT; ++i) {
       const int e = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(sk + lds_off<T::KROW>(e / T::CPR, e % T::CPR)) =
+      const int row = e / T::CPR, c = e % T::CPR;
+      *reinterpret_cast<u32x4*>(sk + row * T::ROW + ((c ^ swz_k<D>(row)) << 4)) =
           kpre[i];
-    }
-    u32x2 tr[8];
-    transpose4x8(vpre, tr);
-    const int pos = (kg >> 2) * 16 + perm_run(kg & 3) * 4;  // key position
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<u32x2*>(sv + lds_off<T::VROW>(dg * 8 + e, pos >> 3) +
-                                (pos & 7) * 2) = tr[e];
+      *reinterpret_cast<u32x4*>(sv + row * T::ROW + ((c ^ swz_v<D>(row)) << 4)) =
+          vpre[i];
     }
   };
+
+  // Loop-invariant per-lane LDS read offsets.
+  // K fragment (A of S^T): row kb*32 + l32, chunk ks*2 + h.
+  int koff[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    koff[ks] = l32 * T::ROW + (((ks * 2 + h) ^ swz_k<D>(l32)) << 4);
+  }
+  // V^T fragment (A of O^T) by transpose reads: source lane s = lane % 16 of
+  // group g = lane / 16 addresses key kk*16 + r2*8 + h*4 + s/4 at column
+  // db*32 + 16*(g & 1) + 4*(s % 4); slots 0-3 (r2 = 0) and 4-7 (r2 = 1) then
+  // hold keys {h*4 + 0..3} and {8 + h*4 + 0..3} of the 16-key group, the
+  // same keys P's registers hold.
+  int voff[T::DB];
+  {
+    const int s16 = lane & 15, g = lane >> 4;
+    const int krow = h * 4 + (s16 >> 2);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 4 * (s16 & 3);
+      voff[db] = krow * T::ROW + (((col >> 3) ^ swz_v<D>(krow)) << 4) +
+                 (col & 7) * 2;
+    }
+  }
 
   f32x16 acc[T::DB];
 #pragma unroll
@@ -180,7 +212,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              sk + lds_off<T::KROW>(kb * 32 + l32, ks * 2 + h));
+              sk + kb * 32 * T::ROW + koff[ks]);
           s[kb] = mfma32(a, qf[ks], s[kb]);
         }
       }
@@ -234,11 +266,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
       // O^T += V^T P^T.
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
+      for (int kk = 0; kk < T::KK; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              sv + lds_off<T::VROW>(db * 32 + l32, kk * 2 + h));
+        for (int db = 0; db < T::DB; ++db) {
+          const unsigned char* pv = sv + kk * 16 * T::ROW + voff[db];
+          const bf16x8 a =
+              join_tr16(lds_read_tr16(pv), lds_read_tr16(pv + 8 * T::ROW));
           acc[db] = mfma32(a, pf[kk], acc[db]);
         }
       }
