@@ -375,8 +375,12 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     if (kt + 1 < kt_end) load_tile(kt + 1);
     const unsigned char* st = smem + stage * T::STAGE;
     const int kbase = kt * T::BCK;
-    if (!CAUSAL || kbase <= qw0 + 31) {
-      // Keys past the end read a valid row and must be masked explicitly.
+    {
+      // No per-wave skip of fully masked tiles here: a uniform branch around
+      // the accumulation makes the compiler copy the accumulators between
+      // register files every iteration, which costs more than the at most
+      // one masked tile per wave it would save.  Keys past the end read a
+      // valid row and are masked explicitly.
       const bool need_mask =
           (CAUSAL && kbase + T::BCK - 1 > qw0) || (kbase + T::BCK > n);
 #pragma unroll
