@@ -82,22 +82,30 @@ void bwd_pre_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
 // ---------------------------------------------------------------------------
 template <int D>
 struct KVTile {
-  static constexpr int NW = 4;
-  static constexpr int BCK = 32 * NW;                 // keys per workgroup
-  static constexpr int BRQ = (D == 128) ? 64 : 128;   // queries per LDS tile
+  static constexpr int NW = 8;                        // waves per workgroup
+  static constexpr int BCK = 128;                     // keys per workgroup
+  static constexpr int BRQ = (D == 128) ? 64 : 128;   // queries per LDS stage
+  static constexpr int QB = BRQ / 32;                 // 32-query blocks per stage
+  static constexpr int QBW = QB / 2;                  // blocks per wave
   static constexpr int KS = D / 16;
-  static constexpr int QB = BRQ / 32;
   static constexpr int DB = D / 32;
-  static constexpr int CPR = D / 8;
   static constexpr int ROW = D * 2;
-  static constexpr int T_BYTES = BRQ * ROW;
-  // stage layout: Q | dO | lse2[BRQ] | D[BRQ]
-  static constexpr int OFF_DO = T_BYTES;
-  static constexpr int OFF_L = 2 * T_BYTES;
-  static constexpr int OFF_D = OFF_L + BRQ * 4;
-  static constexpr int STAGE = OFF_D + BRQ * 4;
-  static constexpr int LPT = BRQ * CPR / 256;
-  static_assert(LPT == 4, "four 16-B chunks of Q and of dO per thread");
+  static constexpr int KV_BYTES = BCK * ROW;          // K (or V) of the workgroup
+  static constexpr int T_BYTES = BRQ * ROW;           // Q (or dO) of one stage
+  // LDS: K | V | stage 0 | stage 1; stage = Q | dO | lse2[BRQ] | D[BRQ]
+  static constexpr int OFF_V = KV_BYTES;
+  static constexpr int OFF_ST = 2 * KV_BYTES;
+  static constexpr int S_DO = T_BYTES;
+  static constexpr int S_L = 2 * T_BYTES;
+  static constexpr int S_D = S_L + BRQ * 4;
+  static constexpr int STAGE = S_D + BRQ * 4;
+  static constexpr int LDS = OFF_ST + 2 * STAGE;
+  static constexpr int KV_BLK = KV_BYTES / 1024 / NW;  // 1-KB DMA blocks per wave
+  static constexpr int T_BLK = T_BYTES / 1024 / NW;
+  static constexpr int RED = 4 * 2 * DB * 16 * 64 * 4;  // partial dK, dV sums
+  static_assert(RED <= LDS, "reduction buffer fits in the tile space");
+  static_assert(KV_BLK * NW * 1024 == KV_BYTES && T_BLK * NW * 1024 == T_BYTES,
+                "tiles split evenly into 1-KB blocks per wave");
 };
 
 // Per-lane offsets of the transposed operand of a 16-row k-step: source lane
@@ -119,8 +127,15 @@ __device__ __forceinline__ void tr_offsets(int lane, int toff[DB][2]) {
   }
 }
 
+// Workgroup of 8 waves = 2 per SIMD.  Wave w owns keys k0 + 32*(w % 4) ..
+// + 31 and the query half w / 4 of every staged query tile; the two waves
+// owning the same keys add their partial dK, dV once at the end.  K and V of
+// the workgroup's 128 keys stay in LDS for its whole life (read as B
+// operands), which keeps the per-wave register footprint within the 256
+// registers that two waves per SIMD allow.  Query tiles are double-buffered
+// and filled by direct global-to-LDS loads.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ ws_d,
@@ -128,102 +143,94 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ dV, int n, int n_ktiles, int total,
                      float c_log2, float scale) {
   using T = KVTile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+  const int kw = w & 3;   // key block of this wave
+  const int qh = w >> 2;  // query half of this wave
 
   const int lid = xcd_logical_id(blockIdx.x, total);
   const int head = lid / n_ktiles;
   const int k0 = (lid % n_ktiles) * T::BCK;  // early key tiles are the heavy ones
   const int64_t hoff = (int64_t)head * n * D;
   const int64_t roff = (int64_t)head * n;
-  const int kw0 = k0 + 32 * w;
+  const int kw0 = k0 + 32 * kw;
   const int key = kw0 + l32;
 
-  // K and V as B operands (lane = key, slots = 8 consecutive d).  Keys past
-  // the end read a valid row; their dK, dV are never stored.
-  bf16x8 kf[T::KS], vf[T::KS];
+  // K and V tiles of the workgroup (rows past the end read row n - 1; their
+  // dK, dV are never stored).
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
-    kf[ks] = as_bf16x8(load_row16(K + hoff, key, n, D, ks * 16 + h * 8));
-    vf[ks] = as_bf16x8(load_row16(V + hoff, key, n, D, ks * 16 + h * 8));
+  for (int i = 0; i < T::KV_BLK; ++i) {
+    dma_tile_block<D>(K + hoff, k0, n, smem, w + T::NW * i, lane);
+    dma_tile_block<D>(V + hoff, k0, n, smem + T::OFF_V, w + T::NW * i, lane);
   }
+
+  const int n_qt = (n + T::BRQ - 1) / T::BRQ;
+  const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
+  // Stage fill: Q and dO tiles (1-KB blocks split over the waves) and the
+  // per-row lse2 and D (one 256-B block per 64 rows, clamped rows; rows past
+  // the end are masked in the math).
+  auto issue_stage = [&](int qt, int stage) {
+    unsigned char* st = smem + T::OFF_ST + stage * T::STAGE;
+    const int q0 = qt * T::BRQ;
+#pragma unroll
+    for (int i = 0; i < T::T_BLK; ++i) {
+      dma_tile_block<D>(Q + hoff, q0, n, st, w + T::NW * i, lane);
+      dma_tile_block<D>(dO + hoff, q0, n, st + T::S_DO, w + T::NW * i, lane);
+    }
+    constexpr int RB = T::BRQ / 64;  // 256-B row blocks per statistic
+    if (w < 2 * RB) {
+      const int which = w / RB, rb = w % RB;
+      const float* src = which ? ws_d : ws_lse2;
+      const int row = min(q0 + rb * 64 + lane, n - 1);
+      dma4(src + roff + row, st + (which ? T::S_D : T::S_L) + rb * 256);
+    }
+  };
+
   f32x16 adk[T::DB], adv[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
     adk[db] = zero16();
     adv[db] = zero16();
   }
-
-  int aoff[T::KS];  // row-wise A operand: row l32 (+ qb*32), chunk ks*2 + h
+  int aoff[T::KS];  // row-wise operand: row l32 (+ 32-row block), chunk ks*2 + h
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) aoff[ks] = tile_off<D>(l32, ks * 2 + h);
   int toff[T::DB][2];
   tr_offsets<D, T::DB>(lane, toff);
-
-  const int n_qt = (n + T::BRQ - 1) / T::BRQ;
-  const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
-
-  // Rows past the end read row n - 1; their lse2 = +inf makes every
-  // rebuilt probability of those rows exactly 0, so they add nothing.
-  u32x4 qpre[T::LPT], dopre[T::LPT];
-  float lpre = 0.f, dpre = 0.f;
-  auto load_tile = [&](int qt) {
-    const int qb0 = qt * T::BRQ;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      qpre[i] = load_row16(Q + hoff, qb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
-      dopre[i] = load_row16(dO + hoff, qb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
-    }
-    if (tid < T::BRQ) {
-      const int row = qb0 + tid;
-      lpre = (row < n) ? ws_lse2[roff + row] : INFINITY;
-      dpre = (row < n) ? ws_d[roff + row] : 0.f;
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned char* st = smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      const int off = tile_off<D>(e / T::CPR, e % T::CPR);
-      *reinterpret_cast<u32x4*>(st + off) = qpre[i];
-      *reinterpret_cast<u32x4*>(st + T::OFF_DO + off) = dopre[i];
-    }
-    if (tid < T::BRQ) {
-      reinterpret_cast<float*>(st + T::OFF_L)[tid] = lpre;
-      reinterpret_cast<float*>(st + T::OFF_D)[tid] = dpre;
-    }
-  };
+  const unsigned char* sk = smem + kw * 32 * T::ROW;
+  const unsigned char* sv = smem + T::OFF_V + kw * 32 * T::ROW;
 
   int stage = 0;
-  if (qt_begin < n_qt) load_tile(qt_begin);
+  if (qt_begin < n_qt) issue_stage(qt_begin, 0);
   for (int qt = qt_begin; qt < n_qt; ++qt) {
-    store_tile(stage);
+    wait_dma();
     __syncthreads();
-    if (qt + 1 < n_qt) load_tile(qt + 1);
-    const unsigned char* st = smem + stage * T::STAGE;
-    const float* sL = reinterpret_cast<const float*>(st + T::OFF_L);
-    const float* sD = reinterpret_cast<const float*>(st + T::OFF_D);
+    if (qt + 1 < n_qt) issue_stage(qt + 1, stage ^ 1);
+    const unsigned char* st = smem + T::OFF_ST + stage * T::STAGE;
+    const float* sL = reinterpret_cast<const float*>(st + T::S_L);
+    const float* sD = reinterpret_cast<const float*>(st + T::S_D);
 #pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
+    for (int qi = 0; qi < T::QBW; ++qi) {
+      const int qb = qh * T::QBW + qi;
       const int qq0 = qt * T::BRQ + qb * 32;
       if (CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
-      // S = Q K^T and dP = dO V^T (M = query, N = key).
+      // S = Q K^T and dP = dO V^T (M = query, N = key), both operands from LDS.
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const unsigned char* pa = st + qb * 32 * T::ROW + aoff[ks];
-        s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kf[ks], s);
-        dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_DO), vf[ks], dp);
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sk + aoff[ks]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sv + aoff[ks]);
+        s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
       }
       // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.
-      const bool need_mask = CAUSAL && qq0 < kw0 + 31;
+      const bool need_mask = (CAUSAL && qq0 < kw0 + 31) || (qq0 + 31 >= n);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 L = *reinterpret_cast<const f32x4*>(sL + qb * 32 + g * 8 + h * 4);
@@ -232,7 +239,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
           float p = fast_exp2(fmaf(s[i], c_log2, -L[t]));
-          if (need_mask && qq0 + g * 8 + h * 4 + t < key) p = 0.f;
+          if (need_mask) {
+            const int q = qq0 + g * 8 + h * 4 + t;
+            if ((CAUSAL && q < key) || q >= n) p = 0.f;
+          }
           s[i] = p;
           dp[i] = p * (dp[i] - Dv[t]);
         }
@@ -246,8 +256,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         const unsigned char* pk = st + (qb * 2 + s2) * 16 * T::ROW;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
-          const bf16x8 a_do = join_tr16(lds_read_tr16(pk + T::OFF_DO + toff[db][0]),
-                                        lds_read_tr16(pk + T::OFF_DO + toff[db][1]));
+          const bf16x8 a_do = join_tr16(lds_read_tr16(pk + T::S_DO + toff[db][0]),
+                                        lds_read_tr16(pk + T::S_DO + toff[db][1]));
           const bf16x8 a_q = join_tr16(lds_read_tr16(pk + toff[db][0]),
                                        lds_read_tr16(pk + toff[db][1]));
           adv[db] = mfma32(a_do, pf[s2], adv[db]);
@@ -258,19 +268,38 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     stage ^= 1;
   }
 
-  // D layout of dK^T / dV^T: lane = key, register i -> d = db*32 + (i/4)*8 + h*4 + i%4.
-  if (key < n) {
+  // Add the two query halves' partial sums through LDS, then store once.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  auto slot = [&](int t, int db, int i) {
+    return ((((kw * 2 + t) * T::DB + db) * 16 + i) * 64) + lane;
+  };
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[slot(0, db, i)] = adk[db][i];
+        red[slot(1, db, i)] = adv[db][i];
+      }
+    }
+  }
+  __syncthreads();
+  if (qh == 0 && key < n) {
     float* dkr = dK + hoff + (int64_t)key * D;
     float* dvr = dV + hoff + (int64_t)key * D;
+    // D layout of dK^T / dV^T: lane = key, register i -> d = db*32 + (i/4)*8 + h*4 + i%4.
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = db * 32 + g * 8 + h * 4;
-        f32x4 xk = {adk[db][4 * g] * scale, adk[db][4 * g + 1] * scale,
-                    adk[db][4 * g + 2] * scale, adk[db][4 * g + 3] * scale};
-        f32x4 xv = {adv[db][4 * g], adv[db][4 * g + 1], adv[db][4 * g + 2],
-                    adv[db][4 * g + 3]};
+        f32x4 xk, xv;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          xk[t] = (adk[db][4 * g + t] + red[slot(0, db, 4 * g + t)]) * scale;
+          xv[t] = adv[db][4 * g + t] + red[slot(1, db, 4 * g + t)];
+        }
         *reinterpret_cast<f32x4*>(dkr + c) = xk;
         *reinterpret_cast<f32x4*>(dvr + c) = xv;
       }
@@ -449,7 +478,7 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = KVTile<D>;
   const int n_kt = (a.n + T::BCK - 1) / T::BCK;
   const int total = (int)(a.bh * n_kt);
-  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3(total), dim3(256), s,
+  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3(total), dim3(512), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,

@@ -126,6 +126,39 @@ __device__ __forceinline__ u32x4 load_row16(const bf16* base, int row, int n,
 }
 
 // ---------------------------------------------------------------------------
+// Global -> LDS direct loads (gfx950 global_load_lds_dwordx4 / _dword).  Lane
+// l of a wave writes its 16 (or 4) bytes at lds + 16*l (4*l): a wave fills
+// one contiguous 1-KB (256-B) block per instruction, and the swizzle of the
+// destination tile is obtained by choosing each lane's source address.  The
+// data lands asynchronously; "s_waitcnt vmcnt(0)" followed by a workgroup
+// barrier makes it visible to every wave.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Fill 1-KB block `blk` of a swizzled row-major tile (rows of D bf16) from
+// global rows row0, row0 + 1, ... of `g` (rows clamped to n - 1).
+template <int D>
+__device__ __forceinline__ void dma_tile_block(const bf16* g, int row0, int n,
+                                               unsigned char* tile, int blk,
+                                               int lane) {
+  const int o = blk * 1024 + lane * 16;
+  const int row = o / (D * 2);
+  const int c = ((o % (D * 2)) >> 4) ^ tile_swz<D>(row);
+  dma16(g + (int64_t)min(row0 + row, n - 1) * D + c * 8, tile + blk * 1024);
+}
+
+// ---------------------------------------------------------------------------
 // Workgroup order.  Consecutive workgroup ids are dealt round-robin over the
 // 8 XCDs, each with its own L2.  Renumbering so that each XCD receives a
 // contiguous range of logical ids keeps all tiles of a head on one XCD, so
