@@ -18,7 +18,7 @@
 // block is 0 are never visited ([XYZ], block-sparse extension).
 //
 // MI355X mapping (one workgroup = 4 waves, wave w owns query rows
-// q0 + 32w .. q0 + 32w + 31):
+// q0 + 32w .. q0 + 32w + 31; two workgroups per CU, two waves per SIMD):
 //   * S is computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //     K comes from LDS as the A operand, Q stays in registers as the B
 //     operand for the whole key loop.  In the D layout each lane then owns a
@@ -31,13 +31,21 @@
 //     and its transposed A operand is read with ds_read_b64_tr_b16; the key
 //     order of those reads matches the key order of P's registers (the
 //     contraction index is a dummy, so both sides only have to agree).
-//   * K and V tiles are double-buffered in LDS (one barrier per tile); the
-//     next tile's global loads are issued before the current tile's math.
-//   * 16-byte chunks are XOR-swizzled per row so that both the row-wise
-//     stores and the fragment reads are free of bank conflicts; every LDS
-//     read address is a loop-invariant per-lane base plus a constant.
+//   * Software pipeline inside each wave: while the matrix cores compute
+//     the score tile of key tile j+1, the vector units turn tile j's scores
+//     into probabilities; then tile j's PV product is issued.  K therefore
+//     runs one tile ahead of V: both are double-buffered in LDS and filled by
+//     direct global-to-LDS loads issued one tile ahead.
+//   * The running max is only moved (and the accumulator rescaled) when a
+//     row's tile max exceeds it by more than 8 in log2 units; any reference
+//     value gives the same quotient, and probabilities stay below 2^8.
+//   * 16-byte chunks are XOR-swizzled per row so that the tile fills and the
+//     fragment reads are free of bank conflicts; LDS read addresses are
+//     loop-invariant per-lane offsets.
 //   * The workgroup order keeps each head on one XCD (shared L2) and, under
 //     the causal rule, starts the longest query tiles first.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -55,10 +63,11 @@ struct FwdTile {
   static constexpr int DB = D / 32;                   // 32-wide blocks of d
   static constexpr int CPR = D / 8;                   // 16-B chunks per row
   static constexpr int ROW = D * 2;                   // bytes per K / V row
-  static constexpr int K_BYTES = BC * ROW;
-  static constexpr int STAGE = 2 * K_BYTES;           // K tile then V tile
-  static constexpr int LPT = BC * CPR / 256;          // chunks per thread
-  static_assert(LPT == 4, "four 16-B chunks of K and of V per thread");
+  static constexpr int K_BYTES = BC * ROW;            // one K or V tile
+  static constexpr int LDS = 4 * K_BYTES;             // K0 | K1 | V0 | V1
+  static constexpr int BLK = K_BYTES / 1024 / NW;     // 1-KB DMA blocks per wave
+  static_assert(BLK * NW * 1024 == K_BYTES, "tile splits into 1-KB blocks");
+  static constexpr float RESCALE_SLACK = 8.f;         // log2 units
 };
 
 // Chunk swizzle of the K tile.  Fragment reads take one chunk from 16
@@ -77,6 +86,23 @@ __device__ __forceinline__ int swz_v(int row) {
   return (D == 128) ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Fill one K or V tile (rows kbase .. kbase + BC - 1, clamped to n - 1) into
+// `tile` with the per-tile chunk swizzle `swz`; wave w moves 1-KB blocks
+// w, w + NW, ...
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
+                                          unsigned char* tile, int w, int lane) {
+  using T = FwdTile<D>;
+#pragma unroll
+  for (int i = 0; i < T::BLK; ++i) {
+    const int blk = w + T::NW * i;
+    const int o = blk * 1024 + lane * 16;
+    const int row = o / T::ROW;
+    const int c = ((o % T::ROW) >> 4) ^ SWZ(row);
+    dma16(g + (int64_t)min(kbase + row, n - 1) * D + c * 8, tile + blk * 1024);
+  }
+}
+
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
@@ -85,7 +111,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float c_log2, const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
+  unsigned char* const kbuf = smem;
+  unsigned char* const vbuf = smem + 2 * T::K_BYTES;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -113,7 +141,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     qf[ks] = as_bf16x8(load_row16(Qh, qrow, n, D, ks * 16 + h * 8));
   }
 
-  // Key tiles to visit.
+  // Key tiles to visit, in order.
   const int n_ktiles = (n + T::BC - 1) / T::BC;
   int kt_end = n_ktiles;
   if (CAUSAL) {
@@ -122,42 +150,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   const uint8_t* mrow =
       SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
-  auto tile_on = [&](int kt) -> bool {
-    return !SPARSE || mrow[(kt * T::BC) / block_n] != 0;
-  };
   auto next_on = [&](int kt) -> int {
     ++kt;
     if constexpr (SPARSE) {
-      while (kt < kt_end && !tile_on(kt)) ++kt;
+      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
     }
     return kt;
-  };
-
-  // Global -> register staging of one K/V tile: thread tid owns chunks
-  // e = tid + 256 i (row e / CPR, chunk e % CPR) of both tiles, so each
-  // quarter-wave stores whole rows (conflict-free under the row swizzles).
-  u32x4 kpre[T::LPT], vpre[T::LPT];
-  auto load_tile = [&](int kt) {
-    const int kbase = kt * T::BC;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      kpre[i] = load_row16(Kh, kbase + e / T::CPR, n, D, (e % T::CPR) * 8);
-      vpre[i] = load_row16(Vh, kbase + e / T::CPR, n, D, (e % T::CPR) * 8);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned char* sk = smem + stage * T::STAGE;
-    unsigned char* sv = sk + T::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      const int row = e / T::CPR, c = e % T::CPR;
-      *reinterpret_cast<u32x4*>(sk + row * T::ROW + ((c ^ swz_k<D>(row)) << 4)) =
-          kpre[i];
-      *reinterpret_cast<u32x4*>(sv + row * T::ROW + ((c ^ swz_v<D>(row)) << 4)) =
-          vpre[i];
-    }
   };
 
   // Loop-invariant per-lane LDS read offsets.
@@ -184,42 +182,65 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   }
 
+  // S^T = K Q^T of the tile in K buffer kb (KB blocks of 32 keys).
+  auto scores = [&](const unsigned char* sk, f32x16 (&s)[T::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      s[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            sk + kb * 32 * T::ROW + koff[ks]);
+        s[kb] = mfma32(a, qf[ks], s[kb]);
+      }
+    }
+  };
+
   f32x16 acc[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) acc[db] = zero16();
-  float m = -INFINITY;  // running max, log2 units of the scaled score
+  float m = -INFINITY;  // reference max, log2 units of the scaled score
   float l = 0.f;        // running exp-sum over this half-wave's keys
 
-  int kt = tile_on(0) ? 0 : next_on(0);
-  if (kt < kt_end) load_tile(kt);
-  int stage = 0;
-  while (kt < kt_end) {
-    store_tile(stage);
+  int cur = next_on(-1);
+  if (cur >= kt_end) goto epilogue;  // (block-sparse) nothing visible
+  {
+    int nxt = next_on(cur);
+    fill_tile<D, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane);
+    fill_tile<D, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane);
+    if (nxt < kt_end) {
+      fill_tile<D, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane);
+    }
+    wait_dma();
     __syncthreads();
-    const int kt_next = next_on(kt);
-    if (kt_next < kt_end) load_tile(kt_next);
+    f32x16 s[T::KB];
+    scores(kbuf, s);
 
-    const unsigned char* sk = smem + stage * T::STAGE;
-    const unsigned char* sv = sk + T::K_BYTES;
-    const int kbase = kt * T::BC;
-    const bool wave_on = !CAUSAL || kbase <= qw0 + 31;
-    if (wave_on) {
-      // S^T = K Q^T for KB blocks of 32 keys.
-      f32x16 s[T::KB];
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        s[kb] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              sk + kb * 32 * T::ROW + koff[ks]);
-          s[kb] = mfma32(a, qf[ks], s[kb]);
+    // One pipeline step for the tile `cur` (scores already in s).  With
+    // NEXT, the scores of tile `nxt` are computed on the matrix cores in the
+    // same basic block as this tile's exponentials, so the two interleave.
+    auto step = [&](auto next_tag, int it) {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      const int kb_cur = it & 1;
+      // Buffers: K of `cur` was in kbuf[kb_cur] (already consumed), K of
+      // `nxt` is in kbuf[kb_cur ^ 1], V of `cur` is in vbuf[kb_cur].
+      wait_dma();
+      __syncthreads();
+      int nxt2 = kt_end;
+      if constexpr (NEXT) {
+        nxt2 = next_on(nxt);
+        if (nxt2 < kt_end) {
+          fill_tile<D, swz_k<D>>(Kh, nxt2 * T::BC, n,
+                                 kbuf + kb_cur * T::K_BYTES, w, lane);
         }
+        fill_tile<D, swz_v<D>>(Vh, nxt * T::BC, n,
+                               vbuf + (kb_cur ^ 1) * T::K_BYTES, w, lane);
       }
-      // Element mask: keys past the diagonal or past the sequence end.
-      const bool need_mask =
-          (CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n);
-      if (need_mask) {
+
+      // Element mask of the current tile: keys past the diagonal or past
+      // the sequence end.
+      const int kbase = cur * T::BC;
+      if ((CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n)) {
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
 #pragma unroll
@@ -229,42 +250,48 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           }
         }
       }
-      // Online softmax update ([TLDR] online softmax; [REAPER] 3.3).
+      // Online softmax ([TLDR] online softmax; [REAPER] 3.3), with the
+      // reference max moved only when the tile max exceeds it by the slack.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m, mx * c_log2);
+      mx = fmaxf(mx, xor32(mx)) * c_log2;
+      const bool move = mx > m + T::RESCALE_SLACK;
+      const float m_new = move ? mx : m;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m - m_use);
-      float rs = 0.f;
-      bf16x8 pf[T::KK];
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
-          s[kb][i] = p;
-          rs += p;
-        }
-        pf[2 * kb] = pack8(s[kb], 0);
-        pf[2 * kb + 1] = pack8(s[kb], 1);
-      }
-      l = l * alpha + rs;
       m = m_new;
-      // alpha == 1 exactly when the row max did not move; skip the multiply
-      // when that holds for the whole wave (an exact shortcut).
-      if (__ballot(alpha != 1.f)) {
+      if (__ballot(move)) {
+        l *= alpha;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
         }
       }
-      // O^T += V^T P^T.
+
+      // Scores of the next tile on the matrix cores while this tile's
+      // probabilities are formed on the vector units.
+      f32x16 s_next[T::KB];
+      if constexpr (NEXT) scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
+      bf16x8 pf[T::KK];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
+          rs += s[kb][i];
+        }
+        pf[2 * kb] = pack8(s[kb], 0);
+        pf[2 * kb + 1] = pack8(s[kb], 1);
+      }
+      l += rs;
+      // O^T += V^T P^T for the current tile.
+      const unsigned char* sv = vbuf + kb_cur * T::K_BYTES;
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
 #pragma unroll
@@ -275,13 +302,21 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           acc[db] = mfma32(a, pf[kk], acc[db]);
         }
       }
-    }
-    stage ^= 1;
-    kt = kt_next;
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) s[kb] = s_next[kb];
+        cur = nxt;
+        nxt = nxt2;
+      }
+    };
+    int it = 0;
+    for (; nxt < kt_end; ++it) step(std::true_type{}, it);
+    step(std::false_type{}, it);
   }
 
-  // Epilogue: one division by l per row ([TLDR] online softmax; [LLMSYS]
-  // Fig. 1: dividing once at the end equals dividing every probability).
+epilogue:
+  // One division by l per row ([TLDR] online softmax; [LLMSYS] Fig. 1:
+  // dividing once at the end equals dividing every probability).
   const float l_tot = l + xor32(l);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < n) {
