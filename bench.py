@@ -47,13 +47,21 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ["fa_fwd_bf16.hip"],
+    "bwd_dkdv_kernel": ["fa_bwd_bf16.hip"],
+    "bwd_dq_kernel": ["fa_bwd_bf16.hip"],
+}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources a kernel is built from (its file + shared headers)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_io_aware_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    files = KERNEL_SOURCES[kernel] + ["fa_device.h", "fa_internal.h"]
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -66,7 +74,7 @@ def stored_traffic(kernel, workload):
     text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
-    if not m_b or not m_h or m_h.group(1) != kernel_source_hash():
+    if not m_b or not m_h or m_h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_b.group(1))
 
@@ -234,7 +242,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0)
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--print-hash", action="store_true",
+                    help="print the source hash of each timed kernel and exit")
     args = ap.parse_args()
+    if args.print_hash:
+        for k in KERNEL_SOURCES:
+            print(k, kernel_source_hash(k))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this "
               "build has no multi-GPU path; the attention kernels shard by "

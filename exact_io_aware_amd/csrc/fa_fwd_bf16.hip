@@ -86,20 +86,41 @@ __device__ __forceinline__ int swz_v(int row) {
   return (D == 128) ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// Fill one K or V tile (rows kbase .. kbase + BC - 1, clamped to n - 1) into
-// `tile` with the per-tile chunk swizzle `swz`; wave w moves 1-KB blocks
-// w, w + NW, ...
+// Source of lane `lane` in 1-KB block i (= w + NW*i) of a K or V tile with
+// chunk swizzle SWZ: the lane fills bytes 16*lane of the block, i.e. row
+// o / ROW, physical chunk (o % ROW) / 16, which holds logical chunk
+// physical ^ SWZ(row).  Returns the element offset from the tile's first
+// row; `row` receives the tile row.
+template <int D, int (*SWZ)(int)>
+__device__ __forceinline__ int tile_src(int w, int lane, int i, int& row) {
+  using T = FwdTile<D>;
+  const int o = (w + T::NW * i) * 1024 + lane * 16;
+  row = o / T::ROW;
+  return row * D + ((((o % T::ROW) >> 4) ^ SWZ(row)) * 8);
+}
+
+// Issue the direct loads of one K or V tile starting at row kbase.  Full
+// tiles use the precomputed per-lane offsets; rows of the last tile at or
+// past n are clamped to n - 1.
 template <int D, int (*SWZ)(int)>
 __device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
-                                          unsigned char* tile, int w, int lane) {
+                                          unsigned char* tile, int w, int lane,
+                                          const int (&off)[FwdTile<D>::BLK]) {
   using T = FwdTile<D>;
+  const bf16* base = g + (int64_t)kbase * D;
+  if (kbase + T::BC <= n) {
 #pragma unroll
-  for (int i = 0; i < T::BLK; ++i) {
-    const int blk = w + T::NW * i;
-    const int o = blk * 1024 + lane * 16;
-    const int row = o / T::ROW;
-    const int c = ((o % T::ROW) >> 4) ^ SWZ(row);
-    dma16(g + (int64_t)min(kbase + row, n - 1) * D + c * 8, tile + blk * 1024);
+    for (int i = 0; i < T::BLK; ++i) {
+      dma16(base + (uint32_t)off[i], tile + (w + T::NW * i) * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::BLK; ++i) {
+      int row;
+      const int o = tile_src<D, SWZ>(w, lane, i, row);
+      const int over = max(kbase + row - (n - 1), 0);  // rows to pull back
+      dma16(base + (o - over * D), tile + (w + T::NW * i) * 1024);
+    }
   }
 }
 
@@ -116,7 +137,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   unsigned char* const vbuf = smem + 2 * T::K_BYTES;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
@@ -129,6 +150,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Qh = Q + hoff;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
+  int koff_g[T::BLK], voff_g[T::BLK];  // per-lane DMA source offsets
+#pragma unroll
+  for (int i = 0; i < T::BLK; ++i) {
+    int row;
+    koff_g[i] = tile_src<D, swz_k<D>>(w, lane, i, row);
+    voff_g[i] = tile_src<D, swz_v<D>>(w, lane, i, row);
+  }
 
   const int qw0 = q0 + 32 * w;   // first query row of this wave
   const int qrow = qw0 + l32;    // query row of this lane
@@ -206,10 +234,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (cur >= kt_end) goto epilogue;  // (block-sparse) nothing visible
   {
     int nxt = next_on(cur);
-    fill_tile<D, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane);
-    fill_tile<D, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane);
+    fill_tile<D, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane, koff_g);
+    fill_tile<D, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane, voff_g);
     if (nxt < kt_end) {
-      fill_tile<D, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane);
+      fill_tile<D, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane, koff_g);
     }
     wait_dma();
     __syncthreads();
@@ -231,10 +259,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         nxt2 = next_on(nxt);
         if (nxt2 < kt_end) {
           fill_tile<D, swz_k<D>>(Kh, nxt2 * T::BC, n,
-                                 kbuf + kb_cur * T::K_BYTES, w, lane);
+                                 kbuf + kb_cur * T::K_BYTES, w, lane, koff_g);
         }
         fill_tile<D, swz_v<D>>(Vh, nxt * T::BC, n,
-                               vbuf + (kb_cur ^ 1) * T::K_BYTES, w, lane);
+                               vbuf + (kb_cur ^ 1) * T::K_BYTES, w, lane, voff_g);
       }
 
       // Element mask of the current tile: keys past the diagonal or past
