@@ -61,7 +61,22 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
 }
 
 // Value held by lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Reductions over the two 32-lane halves of a wave.  v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with both operands equal to x, the two results hold x's lower half
+// twice and its upper half twice, so one max or add gives every lane the
+// combined value (identically in both halves).  A VALU op, unlike a
+// ds_bpermute it needs no LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);

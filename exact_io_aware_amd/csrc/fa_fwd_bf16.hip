@@ -7,7 +7,7 @@
 //   [REAPER] "3 · FlashAttention" (mkdocs.reaper.mx, chapter 3)
 //   [LLMSYS] "출력을 누적해 메모리 이동을 줄이는 FlashAttention"
 //
-// Algorithm: for a block of 128 query rows, stream the key/value tiles
+// Algorithm: for a block of query rows, stream the key/value tiles
 // through LDS; per tile compute the score tile on the matrix cores, update
 // the running row max m, running exp-sum l and the unnormalised output
 // accumulator, and divide by l once after the last tile ([TLDR] online
@@ -17,8 +17,9 @@
 // causal-mask question); in the block-sparse variant key tiles whose mask
 // block is 0 are never visited ([XYZ], block-sparse extension).
 //
-// MI355X mapping (one workgroup = 4 waves, wave w owns query rows
-// q0 + 32w .. q0 + 32w + 31; two workgroups per CU, two waves per SIMD):
+// MI355X mapping (wave w of a workgroup owns query rows q0 + 32w ..
+// q0 + 32w + 31; two waves per SIMD: for d = 128 one workgroup of 8 waves
+// per CU, otherwise two workgroups of 4 waves):
 //   * S is computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //     K comes from LDS as the A operand, Q stays in registers as the B
 //     operand for the whole key loop.  In the D layout each lane then owns a
@@ -33,7 +34,8 @@
 //     contraction index is a dummy, so both sides only have to agree).
 //   * Software pipeline inside each wave: while the matrix cores compute
 //     the score tile of key tile j+1, the vector units turn tile j's scores
-//     into probabilities; then tile j's PV product is issued.  K therefore
+//     into probabilities; while they compute tile j's PV product, the vector
+//     units mask and reduce tile j+1's scores to its row max.  K therefore
 //     runs one tile ahead of V: both are double-buffered in LDS and filled by
 //     direct global-to-LDS loads issued one tile ahead.
 //   * The running max is only moved (and the accumulator rescaled) when a
@@ -52,9 +54,13 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, bool SPARSE>
 struct FwdTile {
-  static constexpr int NW = 4;                        // waves per workgroup
+  // Waves per workgroup: with d = 128 one workgroup of 8 waves per CU
+  // (256 query rows) halves the K/V tile traffic into LDS per query row.
+  // The block-sparse kernel keeps 128 rows, so that a workgroup's rows lie
+  // in one 128-row block row of the mask.
+  static constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   static constexpr int BR = 32 * NW;                  // query rows per workgroup
   static constexpr int BC = (D == 128) ? 64 : 128;    // keys per tile
   static constexpr int KS = D / 16;                   // MFMA k-steps over d
@@ -91,9 +97,9 @@ __device__ __forceinline__ int swz_v(int row) {
 // o / ROW, physical chunk (o % ROW) / 16, which holds logical chunk
 // physical ^ SWZ(row).  Returns the element offset from the tile's first
 // row; `row` receives the tile row.
-template <int D, int (*SWZ)(int)>
+template <class T, int (*SWZ)(int)>
 __device__ __forceinline__ int tile_src(int w, int lane, int i, int& row) {
-  using T = FwdTile<D>;
+  constexpr int D = T::ROW / 2;
   const int o = (w + T::NW * i) * 1024 + lane * 16;
   row = o / T::ROW;
   return row * D + ((((o % T::ROW) >> 4) ^ SWZ(row)) * 8);
@@ -102,11 +108,11 @@ __device__ __forceinline__ int tile_src(int w, int lane, int i, int& row) {
 // Issue the direct loads of one K or V tile starting at row kbase.  Full
 // tiles use the precomputed per-lane offsets; rows of the last tile at or
 // past n are clamped to n - 1.
-template <int D, int (*SWZ)(int)>
+template <class T, int (*SWZ)(int)>
 __device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
                                           unsigned char* tile, int w, int lane,
-                                          const int (&off)[FwdTile<D>::BLK]) {
-  using T = FwdTile<D>;
+                                          const int (&off)[T::BLK]) {
+  constexpr int D = T::ROW / 2;
   const bf16* base = g + (int64_t)kbase * D;
   if (kbase + T::BC <= n) {
 #pragma unroll
@@ -117,7 +123,7 @@ __device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
 #pragma unroll
     for (int i = 0; i < T::BLK; ++i) {
       int row;
-      const int o = tile_src<D, SWZ>(w, lane, i, row);
+      const int o = tile_src<T, SWZ>(w, lane, i, row);
       const int over = max(kbase + row - (n - 1), 0);  // rows to pull back
       dma16(base + (o - over * D), tile + (w + T::NW * i) * 1024);
     }
@@ -125,13 +131,14 @@ __device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((FwdTile<D, SPARSE>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int n, int n_qtiles, int total,
                      float c_log2, const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, SPARSE>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
   unsigned char* const kbuf = smem;
   unsigned char* const vbuf = smem + 2 * T::K_BYTES;
@@ -154,8 +161,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < T::BLK; ++i) {
     int row;
-    koff_g[i] = tile_src<D, swz_k<D>>(w, lane, i, row);
-    voff_g[i] = tile_src<D, swz_v<D>>(w, lane, i, row);
+    koff_g[i] = tile_src<T, swz_k<D>>(w, lane, i, row);
+    voff_g[i] = tile_src<T, swz_v<D>>(w, lane, i, row);
   }
 
   const int qw0 = q0 + 32 * w;   // first query row of this wave
@@ -178,12 +185,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   const uint8_t* mrow =
       SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
+  // (readfirstlane keeps the index opaque to induction-variable rewriting,
+  // which would otherwise turn every DMA source into a loop-carried 64-bit
+  // pointer and exhaust the register file.)
   auto next_on = [&](int kt) -> int {
     ++kt;
     if constexpr (SPARSE) {
       while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
     }
-    return kt;
+    return __builtin_amdgcn_readfirstlane(kt);
   };
 
   // Loop-invariant per-lane LDS read offsets.
@@ -224,31 +234,89 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   };
 
+  // Element mask of a score tile starting at key kbase: keys past the
+  // diagonal or past the sequence end get -inf.  Whether a tile needs it
+  // is wave-uniform.
+  auto needs_mask = [&](int kbase) {
+    return (CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n);
+  };
+  auto apply_mask = [&](f32x16 (&s)[T::KB], int kbase) {
+    // Last visible key of this lane's row, relative to the key held in
+    // register 0 of block 0; register i of block kb holds key
+    // kb*32 + (i/4)*8 + (i%4) relative to it.
+    const int lim = (CAUSAL ? min(qrow, n - 1) : n - 1) - kbase - h * 4;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
+      }
+    }
+  };
+  auto tile_max = [&](const f32x16 (&s)[T::KB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    }
+    return max_halves(mx) * c_log2;
+  };
+
   f32x16 acc[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) acc[db] = zero16();
-  float m = -INFINITY;  // reference max, log2 units of the scaled score
-  float l = 0.f;        // running exp-sum over this half-wave's keys
+  // Online softmax state ([TLDR] online softmax; [REAPER] 3.3).  m is the
+  // reference max in log2 units of the scaled score; it only moves when a
+  // tile max exceeds it by more than the slack.  m_use is m with -inf
+  // replaced by 0, the value subtracted inside the exponentials.
+  float m = -INFINITY;
+  float m_use = 0.f;
+  float l = 0.f;  // running exp-sum over this half-wave's keys
+  // Move the reference max to cover tile max mx; rescale l and the
+  // accumulator when it moves (any lane of the wave).
+  auto move_max = [&](float mx) {
+    const bool move = mx > m + T::RESCALE_SLACK;
+    const float m_new = move ? mx : m;
+    const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
+    if (__ballot(move)) {
+      const float alpha = fast_exp2(m - m_use_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+    }
+    m = m_new;
+    m_use = m_use_new;
+  };
 
   int cur = next_on(-1);
   if (cur >= kt_end) goto epilogue;  // (block-sparse) nothing visible
   {
     int nxt = next_on(cur);
-    fill_tile<D, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane, koff_g);
-    fill_tile<D, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane, voff_g);
+    fill_tile<T, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane, koff_g);
+    fill_tile<T, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane, voff_g);
     if (nxt < kt_end) {
-      fill_tile<D, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane, koff_g);
+      fill_tile<T, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane, koff_g);
     }
     wait_dma();
     __syncthreads();
     f32x16 s[T::KB];
     scores(kbuf, s);
+    if (needs_mask(cur * T::BC)) apply_mask(s, cur * T::BC);
+    move_max(tile_max(s));
 
-    // One pipeline step for the tile `cur` (scores already in s).  With
-    // NEXT, the scores of tile `nxt` are computed on the matrix cores in the
-    // same basic block as this tile's exponentials, so the two interleave.
-    auto step = [&](auto next_tag, int it) {
+    // One pipeline step for tile `cur`, whose scores are in s and whose max
+    // is already folded into m.  Block A: the scores of tile `nxt` on the
+    // matrix cores while the vector units form tile `cur`'s probabilities.
+    // Block B: tile `cur`'s PV product on the matrix cores while the vector
+    // units mask and reduce tile `nxt`'s scores.  MASK_NEXT selects the
+    // masked form of block B, so that each block is one basic block.
+    auto step = [&](auto next_tag, auto mask_tag, int it) {
       constexpr bool NEXT = decltype(next_tag)::value;
+      constexpr bool MASK_NEXT = decltype(mask_tag)::value;
       const int kb_cur = it & 1;
       // Buffers: K of `cur` was in kbuf[kb_cur] (already consumed), K of
       // `nxt` is in kbuf[kb_cur ^ 1], V of `cur` is in vbuf[kb_cur].
@@ -258,51 +326,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       if constexpr (NEXT) {
         nxt2 = next_on(nxt);
         if (nxt2 < kt_end) {
-          fill_tile<D, swz_k<D>>(Kh, nxt2 * T::BC, n,
+          fill_tile<T, swz_k<D>>(Kh, nxt2 * T::BC, n,
                                  kbuf + kb_cur * T::K_BYTES, w, lane, koff_g);
         }
-        fill_tile<D, swz_v<D>>(Vh, nxt * T::BC, n,
+        fill_tile<T, swz_v<D>>(Vh, nxt * T::BC, n,
                                vbuf + (kb_cur ^ 1) * T::K_BYTES, w, lane, voff_g);
       }
 
-      // Element mask of the current tile: keys past the diagonal or past
-      // the sequence end.
-      const int kbase = cur * T::BC;
-      if ((CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n)) {
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-            if ((CAUSAL && key > qrow) || key >= n) s[kb][i] = -INFINITY;
-          }
-        }
-      }
-      // Online softmax ([TLDR] online softmax; [REAPER] 3.3), with the
-      // reference max moved only when the tile max exceeds it by the slack.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      }
-      mx = fmaxf(mx, xor32(mx)) * c_log2;
-      const bool move = mx > m + T::RESCALE_SLACK;
-      const float m_new = move ? mx : m;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      if (__ballot(move)) {
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-      }
-
-      // Scores of the next tile on the matrix cores while this tile's
-      // probabilities are formed on the vector units.
+      // Block A.
       f32x16 s_next[T::KB];
       if constexpr (NEXT) scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
       bf16x8 pf[T::KK];
@@ -318,7 +349,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         pf[2 * kb + 1] = pack8(s[kb], 1);
       }
       l += rs;
-      // O^T += V^T P^T for the current tile.
+
+      // Block B: O^T += V^T P^T for tile `cur`.
       const unsigned char* sv = vbuf + kb_cur * T::K_BYTES;
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
@@ -331,21 +363,30 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
       }
       if constexpr (NEXT) {
+        if constexpr (MASK_NEXT) apply_mask(s_next, nxt * T::BC);
+        move_max(tile_max(s_next));
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) s[kb] = s_next[kb];
         cur = nxt;
         nxt = nxt2;
       }
     };
+    // Tiles needing the element mask come last (keys increase along the
+    // visit order), so the unmasked and masked steps run as two loops.
     int it = 0;
-    for (; nxt < kt_end; ++it) step(std::true_type{}, it);
-    step(std::false_type{}, it);
+#pragma unroll 1
+    for (; nxt < kt_end && !needs_mask(nxt * T::BC); ++it) {
+      step(std::true_type{}, std::false_type{}, it);
+    }
+#pragma unroll 1
+    for (; nxt < kt_end; ++it) step(std::true_type{}, std::true_type{}, it);
+    step(std::false_type{}, std::false_type{}, it);
   }
 
 epilogue:
   // One division by l per row ([TLDR] online softmax; [LLMSYS] Fig. 1:
   // dividing once at the end equals dividing every probability).
-  const float l_tot = l + xor32(l);
+  const float l_tot = sum_halves(l);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < n) {
     bf16* orow = O + hoff + (int64_t)qrow * D;
@@ -368,11 +409,11 @@ epilogue:
 
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t s) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, SPARSE>;
   const int n_qtiles = (a.n + T::BR - 1) / T::BR;
   const int total = (int)(a.bh * n_qtiles);
   return launch_kernel(fwd_bf16_kernel<D, CAUSAL, SPARSE>, dim3(total),
-                       dim3(256), s, (const bf16*)a.q, (const bf16*)a.k,
+                       dim3(T::NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
                        total, a.scale * kLog2e, a.mask, a.mask_cols, a.block_m,
                        a.block_n);
