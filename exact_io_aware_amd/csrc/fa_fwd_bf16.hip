@@ -54,23 +54,18 @@
 namespace fa {
 namespace {
 
-template <int D, bool SPARSE>
+template <int D_, int NW_>
 struct FwdTile {
-  // Waves per workgroup: with d = 128 one workgroup of 8 waves per CU
-  // (256 query rows) halves the K/V tile traffic into LDS per query row.
-  // The block-sparse kernel keeps 128 rows, so that a workgroup's rows lie
-  // in one 128-row block row of the mask.
-  static constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;                      // waves per workgroup
   static constexpr int BR = 32 * NW;                  // query rows per workgroup
   static constexpr int BC = (D == 128) ? 64 : 128;    // keys per tile
   static constexpr int KS = D / 16;                   // MFMA k-steps over d
   static constexpr int KB = BC / 32;                  // 32-key blocks per tile
   static constexpr int KK = BC / 16;                  // 16-key k-steps of PV
   static constexpr int DB = D / 32;                   // 32-wide blocks of d
-  static constexpr int CPR = D / 8;                   // 16-B chunks per row
   static constexpr int ROW = D * 2;                   // bytes per K / V row
   static constexpr int K_BYTES = BC * ROW;            // one K or V tile
-  static constexpr int LDS = 4 * K_BYTES;             // K0 | K1 | V0 | V1
   static constexpr int BLK = K_BYTES / 1024 / NW;     // 1-KB DMA blocks per wave
   static_assert(BLK * NW * 1024 == K_BYTES, "tile splits into 1-KB blocks");
   static constexpr float RESCALE_SLACK = 8.f;         // log2 units
@@ -99,117 +94,98 @@ __device__ __forceinline__ int swz_v(int row) {
 // row; `row` receives the tile row.
 template <class T, int (*SWZ)(int)>
 __device__ __forceinline__ int tile_src(int w, int lane, int i, int& row) {
-  constexpr int D = T::ROW / 2;
   const int o = (w + T::NW * i) * 1024 + lane * 16;
   row = o / T::ROW;
-  return row * D + ((((o % T::ROW) >> 4) ^ SWZ(row)) * 8);
+  return row * T::D + ((((o % T::ROW) >> 4) ^ SWZ(row)) * 8);
 }
 
-// Issue the direct loads of one K or V tile starting at row kbase.  Full
-// tiles use the precomputed per-lane offsets; rows of the last tile at or
-// past n are clamped to n - 1.
-template <class T, int (*SWZ)(int)>
-__device__ __forceinline__ void fill_tile(const bf16* g, int kbase, int n,
-                                          unsigned char* tile, int w, int lane,
-                                          const int (&off)[T::BLK]) {
-  constexpr int D = T::ROW / 2;
-  const bf16* base = g + (int64_t)kbase * D;
-  if (kbase + T::BC <= n) {
-#pragma unroll
-    for (int i = 0; i < T::BLK; ++i) {
-      dma16(base + (uint32_t)off[i], tile + (w + T::NW * i) * 1024);
-    }
-  } else {
+// Direct global-to-LDS fills of K and V tiles: each wave fills BLK of the
+// tile's 1-KB blocks.  Full tiles use precomputed per-lane source offsets;
+// rows of the last tile at or past n are clamped to n - 1.
+template <class T>
+struct TileFill {
+  int koff[T::BLK], voff[T::BLK];
+  int w, lane;
+
+  __device__ __forceinline__ TileFill(int w_, int lane_) : w(w_), lane(lane_) {
 #pragma unroll
     for (int i = 0; i < T::BLK; ++i) {
       int row;
-      const int o = tile_src<T, SWZ>(w, lane, i, row);
-      const int over = max(kbase + row - (n - 1), 0);  // rows to pull back
-      dma16(base + (o - over * D), tile + (w + T::NW * i) * 1024);
+      koff[i] = tile_src<T, swz_k<T::D>>(w, lane, i, row);
+      voff[i] = tile_src<T, swz_v<T::D>>(w, lane, i, row);
     }
   }
-}
-
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__((FwdTile<D, SPARSE>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                     const bf16* __restrict__ V, bf16* __restrict__ O,
-                     float* __restrict__ LSE, int n, int n_qtiles, int total,
-                     float c_log2, const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n) {
-  using T = FwdTile<D, SPARSE>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
-  unsigned char* const kbuf = smem;
-  unsigned char* const vbuf = smem + 2 * T::K_BYTES;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int lane = tid & 63;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int lid = xcd_logical_id(blockIdx.x, total);
-  const int head = lid / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
-  const int q0 = qt * T::BR;
-  const int64_t hoff = (int64_t)head * n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  int koff_g[T::BLK], voff_g[T::BLK];  // per-lane DMA source offsets
+  template <int (*SWZ)(int)>
+  __device__ __forceinline__ void fill(const bf16* g, int kbase, int n,
+                                       unsigned char* tile,
+                                       const int (&off)[T::BLK]) const {
+    const bf16* base = g + (int64_t)kbase * T::D;
+    if (kbase + T::BC <= n) {
 #pragma unroll
-  for (int i = 0; i < T::BLK; ++i) {
-    int row;
-    koff_g[i] = tile_src<T, swz_k<D>>(w, lane, i, row);
-    voff_g[i] = tile_src<T, swz_v<D>>(w, lane, i, row);
-  }
-
-  const int qw0 = q0 + 32 * w;   // first query row of this wave
-  const int qrow = qw0 + l32;    // query row of this lane
-
-  // Q as the B operand of S^T = K Q^T: slot j of k-step ks is
-  // Q[qrow][ks*16 + h*8 + j].
-  bf16x8 qf[T::KS];
+      for (int i = 0; i < T::BLK; ++i) {
+        dma16(base + (uint32_t)off[i], tile + (w + T::NW * i) * 1024);
+      }
+    } else {
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
-    qf[ks] = as_bf16x8(load_row16(Qh, qrow, n, D, ks * 16 + h * 8));
-  }
-
-  // Key tiles to visit, in order.
-  const int n_ktiles = (n + T::BC - 1) / T::BC;
-  int kt_end = n_ktiles;
-  if (CAUSAL) {
-    const int last_q = min(q0 + T::BR, n) - 1;
-    kt_end = min(n_ktiles, last_q / T::BC + 1);
-  }
-  const uint8_t* mrow =
-      SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
-  // (readfirstlane keeps the index opaque to induction-variable rewriting,
-  // which would otherwise turn every DMA source into a loop-carried 64-bit
-  // pointer and exhaust the register file.)
-  auto next_on = [&](int kt) -> int {
-    ++kt;
-    if constexpr (SPARSE) {
-      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
+      for (int i = 0; i < T::BLK; ++i) {
+        int row;
+        const int o = tile_src<T, SWZ>(w, lane, i, row);
+        const int over = max(kbase + row - (n - 1), 0);  // rows to pull back
+        dma16(base + (o - over * T::D), tile + (w + T::NW * i) * 1024);
+      }
     }
-    return __builtin_amdgcn_readfirstlane(kt);
-  };
-
-  // Loop-invariant per-lane LDS read offsets.
-  // K fragment (A of S^T): row kb*32 + l32, chunk ks*2 + h.
-  int koff[T::KS];
-#pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
-    koff[ks] = l32 * T::ROW + (((ks * 2 + h) ^ swz_k<D>(l32)) << 4);
   }
-  // V^T fragment (A of O^T) by transpose reads: source lane s = lane % 16 of
-  // group g = lane / 16 addresses key kk*16 + r2*8 + h*4 + s/4 at column
-  // db*32 + 16*(g & 1) + 4*(s % 4); slots 0-3 (r2 = 0) and 4-7 (r2 = 1) then
-  // hold keys {h*4 + 0..3} and {8 + h*4 + 0..3} of the 16-key group, the
-  // same keys P's registers hold.
-  int voff[T::DB];
-  {
+  __device__ __forceinline__ void k(const bf16* g, int kbase, int n,
+                                    unsigned char* tile) const {
+    fill<swz_k<T::D>>(g, kbase, n, tile, koff);
+  }
+  __device__ __forceinline__ void v(const bf16* g, int kbase, int n,
+                                    unsigned char* tile) const {
+    fill<swz_v<T::D>>(g, kbase, n, tile, voff);
+  }
+};
+
+// The per-wave part of the forward: 32 query rows, their Q fragments, the
+// output accumulator and the online-softmax state ([TLDR] online softmax;
+// [REAPER] 3.3), and the matrix-core and vector steps on one key tile.
+template <class T, bool CAUSAL>
+struct FwdWave {
+  static constexpr int D = T::D;
+  bf16x8 qf[T::KS];    // Q as the B operand of S^T = K Q^T
+  f32x16 acc[T::DB];   // O^T, unnormalised
+  // m is the reference max in log2 units of the scaled score; it only moves
+  // when a tile max exceeds it by more than the slack, and any reference
+  // gives the same quotient.  m_use is m with -inf replaced by 0, the value
+  // subtracted inside the exponentials; l is the running exp-sum over this
+  // half-wave's keys.
+  float m, m_use, l;
+  int koff[T::KS];     // K fragment LDS offsets
+  int voff[T::DB];     // V^T fragment (transpose read) LDS offsets
+  int qw0, qrow, h, n;
+  float c_log2;
+
+  __device__ __forceinline__ FwdWave(const bf16* Qh, int qw0_, int lane, int n_,
+                                     float c_log2_)
+      : m(-INFINITY), m_use(0.f), l(0.f), qw0(qw0_), qrow(qw0_ + (lane & 31)),
+        h(lane >> 5), n(n_), c_log2(c_log2_) {
+    const int l32 = lane & 31;
+    // Slot j of k-step ks is Q[qrow][ks*16 + h*8 + j].
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      qf[ks] = as_bf16x8(load_row16(Qh, qrow, n, D, ks * 16 + h * 8));
+    }
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) acc[db] = zero16();
+    // K fragment (A of S^T): row kb*32 + l32, chunk ks*2 + h.
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      koff[ks] = l32 * T::ROW + (((ks * 2 + h) ^ swz_k<D>(l32)) << 4);
+    }
+    // V^T fragment (A of O^T) by transpose reads: source lane s = lane % 16
+    // of group g = lane / 16 addresses key kk*16 + r2*8 + h*4 + s/4 at
+    // column db*32 + 16*(g & 1) + 4*(s % 4); slots 0-3 (r2 = 0) and 4-7
+    // (r2 = 1) then hold keys {h*4 + 0..3} and {8 + h*4 + 0..3} of the
+    // 16-key group, the same keys P's registers hold.
     const int s16 = lane & 15, g = lane >> 4;
     const int krow = h * 4 + (s16 >> 2);
 #pragma unroll
@@ -220,8 +196,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   }
 
-  // S^T = K Q^T of the tile in K buffer kb (KB blocks of 32 keys).
-  auto scores = [&](const unsigned char* sk, f32x16 (&s)[T::KB]) {
+  // S^T = K Q^T of the K tile at sk (KB blocks of 32 keys).
+  __device__ __forceinline__ void scores(const unsigned char* sk,
+                                         f32x16 (&s)[T::KB]) const {
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       s[kb] = zero16();
@@ -232,18 +209,18 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         s[kb] = mfma32(a, qf[ks], s[kb]);
       }
     }
-  };
+  }
 
-  // Element mask of a score tile starting at key kbase: keys past the
-  // diagonal or past the sequence end get -inf.  Whether a tile needs it
-  // is wave-uniform.
-  auto needs_mask = [&](int kbase) {
+  // Whether the tile starting at key kbase has keys past the diagonal or
+  // past the sequence end for some row of this wave (wave-uniform).
+  __device__ __forceinline__ bool needs_mask(int kbase) const {
     return (CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n);
-  };
-  auto apply_mask = [&](f32x16 (&s)[T::KB], int kbase) {
-    // Last visible key of this lane's row, relative to the key held in
-    // register 0 of block 0; register i of block kb holds key
-    // kb*32 + (i/4)*8 + (i%4) relative to it.
+  }
+  // Set those keys to -inf.  lim is the last visible key of the lane's row
+  // relative to the key in register 0 of block 0; register i of block kb
+  // holds key kb*32 + (i/4)*8 + (i%4) relative to it.
+  __device__ __forceinline__ void apply_mask(f32x16 (&s)[T::KB],
+                                             int kbase) const {
     const int lim = (CAUSAL ? min(qrow, n - 1) : n - 1) - kbase - h * 4;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
@@ -252,8 +229,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
       }
     }
-  };
-  auto tile_max = [&](const f32x16 (&s)[T::KB]) {
+  }
+  // Row max of a score tile in log2 units.
+  __device__ __forceinline__ float tile_max(const f32x16 (&s)[T::KB]) const {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
@@ -261,21 +239,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     }
     return max_halves(mx) * c_log2;
-  };
-
-  f32x16 acc[T::DB];
-#pragma unroll
-  for (int db = 0; db < T::DB; ++db) acc[db] = zero16();
-  // Online softmax state ([TLDR] online softmax; [REAPER] 3.3).  m is the
-  // reference max in log2 units of the scaled score; it only moves when a
-  // tile max exceeds it by more than the slack.  m_use is m with -inf
-  // replaced by 0, the value subtracted inside the exponentials.
-  float m = -INFINITY;
-  float m_use = 0.f;
-  float l = 0.f;  // running exp-sum over this half-wave's keys
+  }
   // Move the reference max to cover tile max mx; rescale l and the
   // accumulator when it moves (any lane of the wave).
-  auto move_max = [&](float mx) {
+  __device__ __forceinline__ void move_max(float mx) {
     const bool move = mx > m + T::RESCALE_SLACK;
     const float m_new = move ? mx : m;
     const float m_use_new = (m_new == -INFINITY) ? 0.f : m_new;
@@ -290,106 +257,45 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     m = m_new;
     m_use = m_use_new;
-  };
-
-  int cur = next_on(-1);
-  if (cur >= kt_end) goto epilogue;  // (block-sparse) nothing visible
-  {
-    int nxt = next_on(cur);
-    fill_tile<T, swz_k<D>>(Kh, cur * T::BC, n, kbuf, w, lane, koff_g);
-    fill_tile<T, swz_v<D>>(Vh, cur * T::BC, n, vbuf, w, lane, voff_g);
-    if (nxt < kt_end) {
-      fill_tile<T, swz_k<D>>(Kh, nxt * T::BC, n, kbuf + T::K_BYTES, w, lane, koff_g);
-    }
-    wait_dma();
-    __syncthreads();
-    f32x16 s[T::KB];
-    scores(kbuf, s);
-    if (needs_mask(cur * T::BC)) apply_mask(s, cur * T::BC);
-    move_max(tile_max(s));
-
-    // One pipeline step for tile `cur`, whose scores are in s and whose max
-    // is already folded into m.  Block A: the scores of tile `nxt` on the
-    // matrix cores while the vector units form tile `cur`'s probabilities.
-    // Block B: tile `cur`'s PV product on the matrix cores while the vector
-    // units mask and reduce tile `nxt`'s scores.  MASK_NEXT selects the
-    // masked form of block B, so that each block is one basic block.
-    auto step = [&](auto next_tag, auto mask_tag, int it) {
-      constexpr bool NEXT = decltype(next_tag)::value;
-      constexpr bool MASK_NEXT = decltype(mask_tag)::value;
-      const int kb_cur = it & 1;
-      // Buffers: K of `cur` was in kbuf[kb_cur] (already consumed), K of
-      // `nxt` is in kbuf[kb_cur ^ 1], V of `cur` is in vbuf[kb_cur].
-      wait_dma();
-      __syncthreads();
-      int nxt2 = kt_end;
-      if constexpr (NEXT) {
-        nxt2 = next_on(nxt);
-        if (nxt2 < kt_end) {
-          fill_tile<T, swz_k<D>>(Kh, nxt2 * T::BC, n,
-                                 kbuf + kb_cur * T::K_BYTES, w, lane, koff_g);
-        }
-        fill_tile<T, swz_v<D>>(Vh, nxt * T::BC, n,
-                               vbuf + (kb_cur ^ 1) * T::K_BYTES, w, lane, voff_g);
-      }
-
-      // Block A.
-      f32x16 s_next[T::KB];
-      if constexpr (NEXT) scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
-      bf16x8 pf[T::KK];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
-          rs += s[kb][i];
-        }
-        pf[2 * kb] = pack8(s[kb], 0);
-        pf[2 * kb + 1] = pack8(s[kb], 1);
-      }
-      l += rs;
-
-      // Block B: O^T += V^T P^T for tile `cur`.
-      const unsigned char* sv = vbuf + kb_cur * T::K_BYTES;
-#pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk) {
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-          const unsigned char* pv = sv + kk * 16 * T::ROW + voff[db];
-          const bf16x8 a =
-              join_tr16(lds_read_tr16(pv), lds_read_tr16(pv + 8 * T::ROW));
-          acc[db] = mfma32(a, pf[kk], acc[db]);
-        }
-      }
-      if constexpr (NEXT) {
-        if constexpr (MASK_NEXT) apply_mask(s_next, nxt * T::BC);
-        move_max(tile_max(s_next));
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) s[kb] = s_next[kb];
-        cur = nxt;
-        nxt = nxt2;
-      }
-    };
-    // Tiles needing the element mask come last (keys increase along the
-    // visit order), so the unmasked and masked steps run as two loops.
-    int it = 0;
-#pragma unroll 1
-    for (; nxt < kt_end && !needs_mask(nxt * T::BC); ++it) {
-      step(std::true_type{}, std::false_type{}, it);
-    }
-#pragma unroll 1
-    for (; nxt < kt_end; ++it) step(std::true_type{}, std::true_type{}, it);
-    step(std::false_type{}, std::false_type{}, it);
   }
-
-epilogue:
+  // Probabilities exp2(S*c - m) into the B-operand layout of the PV product
+  // (bf16), and their fp32 row sum into l.
+  __device__ __forceinline__ void probs(f32x16 (&s)[T::KB],
+                                        bf16x8 (&pf)[T::KK]) {
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
+        rs += s[kb][i];
+      }
+      pf[2 * kb] = pack8(s[kb], 0);
+      pf[2 * kb + 1] = pack8(s[kb], 1);
+    }
+    l += rs;
+  }
+  // O^T += V^T P^T for the V tile at sv.
+  __device__ __forceinline__ void pv(const unsigned char* sv,
+                                     const bf16x8 (&pf)[T::KK]) {
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) {
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const unsigned char* p = sv + kk * 16 * T::ROW + voff[db];
+        const bf16x8 a = join_tr16(lds_read_tr16(p), lds_read_tr16(p + 8 * T::ROW));
+        acc[db] = mfma32(a, pf[kk], acc[db]);
+      }
+    }
+  }
   // One division by l per row ([TLDR] online softmax; [LLMSYS] Fig. 1:
-  // dividing once at the end equals dividing every probability).
-  const float l_tot = sum_halves(l);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (qrow < n) {
-    bf16* orow = O + hoff + (int64_t)qrow * D;
+  // dividing once at the end equals dividing every probability), and
+  // LSE = m + ln l in natural-log units.
+  __device__ __forceinline__ void store(bf16* Oh, float* lse_h) const {
+    const float l_tot = sum_halves(l);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow >= n) return;
+    bf16* orow = Oh + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
@@ -401,19 +307,136 @@ epilogue:
       }
     }
     if (h == 0) {
-      LSE[(int64_t)head * n + qrow] =
-          (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      lse_h[qrow] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }
+};
+
+// Workgroup coordinates (head, first query row).
+struct FwdPlace {
+  int head, q0;
+};
+template <bool CAUSAL>
+__device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br) {
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  return {lid / n_qtiles, qt * br};
+}
+
+// Every wave runs the same pipeline step per key tile:
+//   block A: the scores of tile `nxt` on the matrix cores while the vector
+//            units form tile `cur`'s probabilities;
+//   block B: tile `cur`'s PV product on the matrix cores while the vector
+//            units mask and reduce tile `nxt`'s scores.
+// With d = 128 (dense) a workgroup has 8 waves, one workgroup per CU: 256
+// query rows share each K/V tile, halving the tile traffic into LDS per row.
+// Otherwise a workgroup has 4 waves and two run per CU; the block-sparse
+// kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
+// row of the mask.
+template <int D, int NW, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, bf16* __restrict__ O,
+                     float* __restrict__ LSE, int n, int n_qtiles, int total,
+                     float c_log2, const uint8_t* __restrict__ mask,
+                     int mask_cols, int block_m, int block_n) {
+  using T = FwdTile<D, NW>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
+  unsigned char* const kbuf = smem;                  // K0 | K1
+  unsigned char* const vbuf = smem + 2 * T::K_BYTES;  // V0 | V1
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR);
+  const int64_t hoff = (int64_t)pl.head * n * D;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const TileFill<T> fill(w, lane);
+  FwdWave<T, CAUSAL> wv(Q + hoff, pl.q0 + 32 * w, lane, n, c_log2);
+
+  // Key tiles to visit, in order.
+  const int n_ktiles = (n + T::BC - 1) / T::BC;
+  int kt_end = n_ktiles;
+  if (CAUSAL) kt_end = min(n_ktiles, (min(pl.q0 + T::BR, n) - 1) / T::BC + 1);
+  const uint8_t* mrow =
+      SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : nullptr;
+  // (readfirstlane keeps the index opaque to induction-variable rewriting,
+  // which would otherwise turn every DMA source into a loop-carried 64-bit
+  // pointer and exhaust the register file.)
+  auto next_on = [&](int kt) -> int {
+    ++kt;
+    if constexpr (SPARSE) {
+      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
+    }
+    return __builtin_amdgcn_readfirstlane(kt);
+  };
+
+  int cur = next_on(-1);
+  if (cur < kt_end) {
+    int nxt = next_on(cur);
+    fill.k(Kh, cur * T::BC, n, kbuf);
+    fill.v(Vh, cur * T::BC, n, vbuf);
+    if (nxt < kt_end) fill.k(Kh, nxt * T::BC, n, kbuf + T::K_BYTES);
+    wait_dma();
+    __syncthreads();
+    f32x16 s[T::KB];
+    wv.scores(kbuf, s);
+    if (wv.needs_mask(cur * T::BC)) wv.apply_mask(s, cur * T::BC);
+    wv.move_max(wv.tile_max(s));
+
+    // One step for tile `cur`, whose scores are in s and whose max is
+    // already in m.  MASK_NEXT selects the masked form of block B, so that
+    // each block is one basic block.
+    auto step = [&](auto next_tag, auto mask_tag, int it) {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      constexpr bool MASK_NEXT = decltype(mask_tag)::value;
+      const int kb_cur = it & 1;
+      // K of `cur` was in kbuf[kb_cur] (already consumed), K of `nxt` is in
+      // kbuf[kb_cur ^ 1], V of `cur` is in vbuf[kb_cur].
+      wait_dma();
+      __syncthreads();
+      int nxt2 = kt_end;
+      if constexpr (NEXT) {
+        nxt2 = next_on(nxt);
+        if (nxt2 < kt_end) fill.k(Kh, nxt2 * T::BC, n, kbuf + kb_cur * T::K_BYTES);
+        fill.v(Vh, nxt * T::BC, n, vbuf + (kb_cur ^ 1) * T::K_BYTES);
+      }
+      f32x16 s_next[T::KB];
+      if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
+      bf16x8 pf[T::KK];
+      wv.probs(s, pf);
+      wv.pv(vbuf + kb_cur * T::K_BYTES, pf);
+      if constexpr (NEXT) {
+        if constexpr (MASK_NEXT) wv.apply_mask(s_next, nxt * T::BC);
+        wv.move_max(wv.tile_max(s_next));
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) s[kb] = s_next[kb];
+        cur = nxt;
+        nxt = nxt2;
+      }
+    };
+    // Tiles needing the element mask come last (keys increase along the
+    // visit order), so the unmasked and masked steps run as two loops.
+    int it = 0;
+#pragma unroll 1
+    for (; nxt < kt_end && !wv.needs_mask(nxt * T::BC); ++it) {
+      step(std::true_type{}, std::false_type{}, it);
+    }
+#pragma unroll 1
+    for (; nxt < kt_end; ++it) step(std::true_type{}, std::true_type{}, it);
+    step(std::false_type{}, std::false_type{}, it);
+  }
+  wv.store(O + hoff, LSE + (int64_t)pl.head * n);
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t s) {
-  using T = FwdTile<D, SPARSE>;
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
+  using T = FwdTile<D, NW>;
   const int n_qtiles = (a.n + T::BR - 1) / T::BR;
   const int total = (int)(a.bh * n_qtiles);
-  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, SPARSE>, dim3(total),
-                       dim3(T::NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
+  return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
+                       dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
                        total, a.scale * kLog2e, a.mask, a.mask_cols, a.block_m,
                        a.block_n);
@@ -422,11 +445,11 @@ hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
   if (a.mask) {
-    return a.causal ? launch_fwd_bf16_t<D, true, true>(a, s)
-                    : launch_fwd_bf16_t<D, false, true>(a, s);
+    return a.causal ? launch_fwd<D, true, true>(a, s)
+                    : launch_fwd<D, false, true>(a, s);
   }
-  return a.causal ? launch_fwd_bf16_t<D, true, false>(a, s)
-                  : launch_fwd_bf16_t<D, false, false>(a, s);
+  return a.causal ? launch_fwd<D, true, false>(a, s)
+                  : launch_fwd<D, false, false>(a, s);
 }
 
 }  // namespace
