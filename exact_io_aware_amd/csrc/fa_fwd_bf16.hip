@@ -379,18 +379,25 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     if (nxt < kt_end) fill.k(Kh, nxt * T::BC, n, kbuf + T::K_BYTES);
     wait_dma();
     __syncthreads();
-    f32x16 s[T::KB];
-    wv.scores(kbuf, s);
-    if (wv.needs_mask(cur * T::BC)) wv.apply_mask(s, cur * T::BC);
-    wv.move_max(wv.tile_max(s));
+    // sa holds the current tile's scores; the next tile's scores go to sb
+    // (and the roles swap) in the unrolled loop, so no copy is needed there.
+    f32x16 sa[T::KB], sb[T::KB];
+    wv.scores(kbuf, sa);
+    if (wv.needs_mask(cur * T::BC)) wv.apply_mask(sa, cur * T::BC);
+    wv.move_max(wv.tile_max(sa));
 
     // One step for tile `cur`, whose scores are in s and whose max is
-    // already in m.  MASK_NEXT selects the masked form of block B, so that
-    // each block is one basic block.
-    auto step = [&](auto next_tag, auto mask_tag, int it) {
+    // already in m; the scores of tile `nxt` go to s_next.  MASK_NEXT
+    // selects the masked form of block B, so that each block is one basic
+    // block.  PAR is the LDS buffer parity of `cur` when it is known at
+    // compile time (then every LDS address is a register plus an immediate),
+    // or -1 to take it from the step count.
+    auto step = [&](auto next_tag, auto mask_tag, auto par_tag, int it,
+                    f32x16 (&s)[T::KB], f32x16 (&s_next)[T::KB]) {
       constexpr bool NEXT = decltype(next_tag)::value;
       constexpr bool MASK_NEXT = decltype(mask_tag)::value;
-      const int kb_cur = it & 1;
+      constexpr int PAR = decltype(par_tag)::value;
+      const int kb_cur = (PAR >= 0) ? PAR : (it & 1);
       // K of `cur` was in kbuf[kb_cur] (already consumed), K of `nxt` is in
       // kbuf[kb_cur ^ 1], V of `cur` is in vbuf[kb_cur].
       wait_dma();
@@ -401,7 +408,6 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (nxt2 < kt_end) fill.k(Kh, nxt2 * T::BC, n, kbuf + kb_cur * T::K_BYTES);
         fill.v(Vh, nxt * T::BC, n, vbuf + (kb_cur ^ 1) * T::K_BYTES);
       }
-      f32x16 s_next[T::KB];
       if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
       bf16x8 pf[T::KK];
       wv.probs(s, pf);
@@ -409,22 +415,40 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       if constexpr (NEXT) {
         if constexpr (MASK_NEXT) wv.apply_mask(s_next, nxt * T::BC);
         wv.move_max(wv.tile_max(s_next));
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) s[kb] = s_next[kb];
         cur = nxt;
         nxt = nxt2;
       }
     };
+    using yes = std::true_type;
+    using no = std::false_type;
+    using par0 = std::integral_constant<int, 0>;
+    using par1 = std::integral_constant<int, 1>;
+    using par_rt = std::integral_constant<int, -1>;
+    auto copy_b_to_a = [&]() {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) sa[kb] = sb[kb];
+    };
     // Tiles needing the element mask come last (keys increase along the
-    // visit order), so the unmasked and masked steps run as two loops.
+    // visit order).  Unmasked steps run in pairs (parity 0 then 1, scores
+    // in sa then sb); the rest take the parity from the step count.
     int it = 0;
 #pragma unroll 1
-    for (; nxt < kt_end && !wv.needs_mask(nxt * T::BC); ++it) {
-      step(std::true_type{}, std::false_type{}, it);
+    while (nxt < kt_end && !wv.needs_mask(nxt * T::BC)) {
+      step(yes{}, no{}, par0{}, it, sa, sb);
+      ++it;
+      if (!(nxt < kt_end && !wv.needs_mask(nxt * T::BC))) {
+        copy_b_to_a();
+        break;
+      }
+      step(yes{}, no{}, par1{}, it, sb, sa);
+      ++it;
     }
 #pragma unroll 1
-    for (; nxt < kt_end; ++it) step(std::true_type{}, std::true_type{}, it);
-    step(std::false_type{}, std::false_type{}, it);
+    for (; nxt < kt_end; ++it) {
+      step(yes{}, yes{}, par_rt{}, it, sa, sb);
+      copy_b_to_a();
+    }
+    step(no{}, no{}, par_rt{}, it, sa, sb);
   }
   wv.store(O + hoff, LSE + (int64_t)pl.head * n);
 }
