@@ -32,6 +32,8 @@
 // those same tiles, with one XOR swizzle that is conflict-free for both the
 // row-wise and the transposed read pattern.  Causal key/query tiles that are
 // fully masked are skipped ([REAPER], causal-mask question).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -310,37 +312,40 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW_>
 struct QTile {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;
   static constexpr int BRQ = 32 * NW;                 // queries per workgroup
   static constexpr int BCK = (D == 128) ? 64 : 128;   // keys per LDS tile
   static constexpr int KS = D / 16;
   static constexpr int KB = BCK / 32;
   static constexpr int DB = D / 32;
-  static constexpr int CPR = D / 8;
   static constexpr int ROW = D * 2;
   static constexpr int T_BYTES = BCK * ROW;
-  // stage layout: K | V
+  // stage layout: K | V, two stages
   static constexpr int OFF_V = T_BYTES;
   static constexpr int STAGE = 2 * T_BYTES;
-  static constexpr int LPT = BCK * CPR / 256;
-  static_assert(LPT == 4, "four 16-B chunks of K and of V per thread");
+  static constexpr int BLK = T_BYTES / 1024 / NW;     // 1-KB DMA blocks per wave
+  static_assert(BLK * NW * 1024 == T_BYTES, "tile splits into 1-KB blocks");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+// With d = 128 a workgroup has 8 waves (256 queries, one workgroup per CU),
+// which halves the K/V tile traffic into LDS per query row; with d = 64 it
+// has 4 waves and two run per CU.  Wave w owns queries q0 + 32w .. + 31; Q
+// and dO stay in registers as B operands.  K/V tiles are double-buffered
+// and filled by direct global-to-LDS loads one tile ahead.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ ws_d,
                    const float* __restrict__ ws_lse2, float* __restrict__ dQ,
                    int n, int n_qtiles, int total, float c_log2, float scale) {
-  using T = QTile<D>;
+  using T = QTile<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -349,6 +354,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
   const int q0 = qt * T::BRQ;
   const int64_t hoff = (int64_t)head * n * D;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
 
@@ -370,83 +377,118 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   for (int ks = 0; ks < T::KS; ++ks) aoff[ks] = tile_off<D>(l32, ks * 2 + h);
   int toff[T::DB][2];
   tr_offsets<D, T::DB>(lane, toff);
+  // DMA sources: lane `lane` fills bytes 16*lane of 1-KB block w + NW*i of a
+  // tile, i.e. row o / ROW, physical chunk (o % ROW) / 16 = logical chunk ^
+  // swizzle; element offsets from the tile's first row.
+  int goff[T::BLK];
+#pragma unroll
+  for (int i = 0; i < T::BLK; ++i) {
+    const int o = (w + NW * i) * 1024 + lane * 16;
+    const int row = o / T::ROW;
+    goff[i] = row * D + ((((o % T::ROW) >> 4) ^ tile_swz<D>(row)) * 8);
+  }
+  auto fill = [&](int kt, int stage) {
+    unsigned char* st = smem + stage * T::STAGE;
+    const int kb0 = kt * T::BCK;
+    const bf16* kbase = Kh + (int64_t)kb0 * D;
+    const bf16* vbase = Vh + (int64_t)kb0 * D;
+    if (kb0 + T::BCK <= n) {
+#pragma unroll
+      for (int i = 0; i < T::BLK; ++i) {
+        dma16(kbase + (uint32_t)goff[i], st + (w + NW * i) * 1024);
+        dma16(vbase + (uint32_t)goff[i], st + T::OFF_V + (w + NW * i) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::BLK; ++i) {
+        dma_tile_block<D>(Kh, kb0, n, st, w + NW * i, lane);
+        dma_tile_block<D>(Vh, kb0, n, st + T::OFF_V, w + NW * i, lane);
+      }
+    }
+  };
 
   const int n_kt = (n + T::BCK - 1) / T::BCK;
-  int kt_end = n_kt;
-  if (CAUSAL) kt_end = min(n_kt, (min(q0 + T::BRQ, n) - 1) / T::BCK + 1);
-
-  u32x4 kpre[T::LPT], vpre[T::LPT];
-  auto load_tile = [&](int kt) {
-    const int kb0 = kt * T::BCK;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      kpre[i] = load_row16(K + hoff, kb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
-      vpre[i] = load_row16(V + hoff, kb0 + e / T::CPR, n, D, (e % T::CPR) * 8);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned char* st = smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::LPT; ++i) {
-      const int e = tid + 256 * i;
-      const int off = tile_off<D>(e / T::CPR, e % T::CPR);
-      *reinterpret_cast<u32x4*>(st + off) = kpre[i];
-      *reinterpret_cast<u32x4*>(st + T::OFF_V + off) = vpre[i];
-    }
+  const int kt_end =
+      CAUSAL ? min(n_kt, (min(q0 + T::BRQ, n) - 1) / T::BCK + 1) : n_kt;
+  // Whether tile kt has keys after some query of this wave or past the end.
+  auto needs_mask = [&](int kt) {
+    const int kbase = kt * T::BCK;
+    return (CAUSAL && kbase + T::BCK - 1 > qw0) || (kbase + T::BCK > n);
   };
 
-  int stage = 0;
-  if (kt_end > 0) load_tile(0);
-  for (int kt = 0; kt < kt_end; ++kt) {
-    store_tile(stage);
+  // One key tile: wait for it (loaded one tile ahead) and let every wave
+  // finish the previous one, load the next tile into the freed stage, then
+  // accumulate dQ^T.  PAR is the stage parity when known at compile time
+  // (every LDS address is then a register plus an immediate), else -1.
+  auto tile = [&](auto mask_tag, auto par_tag, int kt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    const int stage = (PAR >= 0) ? PAR : (kt & 1);
+    wait_dma();
     __syncthreads();
-    if (kt + 1 < kt_end) load_tile(kt + 1);
+    if (kt + 1 < kt_end) fill(kt + 1, stage ^ 1);
     const unsigned char* st = smem + stage * T::STAGE;
     const int kbase = kt * T::BCK;
-    {
-      // No per-wave skip of fully masked tiles here: a uniform branch around
-      // the accumulation makes the compiler copy the accumulators between
-      // register files every iteration, which costs more than the at most
-      // one masked tile per wave it would save.  Keys past the end read a
-      // valid row and are masked explicitly.
-      const bool need_mask =
-          (CAUSAL && kbase + T::BCK - 1 > qw0) || (kbase + T::BCK > n);
+    // Last visible key of this lane's row relative to the key in register 0
+    // of block 0 (register i of block kb holds key kb*32 + (i/4)*8 + i%4
+    // relative to it).
+    const int lim = (CAUSAL ? min(qrow, n - 1) : n - 1) - kbase - h * 4;
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
-        f32x16 s = zero16(), dp = zero16();
+    for (int kb = 0; kb < T::KB; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-          const unsigned char* pa = st + kb * 32 * T::ROW + aoff[ks];
-          s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const unsigned char* pa = st + kb * 32 * T::ROW + aoff[ks];
+        s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
+        if constexpr (MASK) {
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) p = 0.f;
         }
+        dp[i] = p * (dp[i] - drow);
+      }
+      const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
+      // dQ^T += K^T dS^T (M = d, N = query, K = key); K^T from transpose
+      // reads of the K tile.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
-          if (need_mask) {
-            const int kj = kbase + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-            if ((CAUSAL && kj > qrow) || kj >= n) p = 0.f;
-          }
-          dp[i] = p * (dp[i] - drow);
-        }
-        const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
-        // dQ^T += K^T dS^T (M = d, N = query, K = key); K^T from transpose
-        // reads of the K tile.
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const unsigned char* pk = st + (kb * 2 + s2) * 16 * T::ROW;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const unsigned char* pk = st + (kb * 2 + s2) * 16 * T::ROW;
-#pragma unroll
-          for (int db = 0; db < T::DB; ++db) {
-            const bf16x8 a = join_tr16(lds_read_tr16(pk + toff[db][0]),
-                                       lds_read_tr16(pk + toff[db][1]));
-            adq[db] = mfma32(a, sf[s2], adq[db]);
-          }
+        for (int db = 0; db < T::DB; ++db) {
+          const bf16x8 a = join_tr16(lds_read_tr16(pk + toff[db][0]),
+                                     lds_read_tr16(pk + toff[db][1]));
+          adq[db] = mfma32(a, sf[s2], adq[db]);
         }
       }
     }
-    stage ^= 1;
+  };
+
+  using yes = std::true_type;
+  using no = std::false_type;
+  using par0 = std::integral_constant<int, 0>;
+  using par1 = std::integral_constant<int, 1>;
+  using par_rt = std::integral_constant<int, -1>;
+  if (kt_end > 0) {
+    fill(0, 0);
+    // Tiles needing the element mask come last; unmasked tiles run in
+    // pairs with static stage parity.
+    int kt = 0;
+#pragma unroll 1
+    while (kt + 1 < kt_end && !needs_mask(kt + 1)) {
+      tile(no{}, par0{}, kt);
+      tile(no{}, par1{}, kt + 1);
+      kt = __builtin_amdgcn_readfirstlane(kt + 2);
+    }
+    // (At most one unmasked tile remains here; it takes the masked form,
+    // whose mask is then a no-op.)
+#pragma unroll 1
+    for (; kt < kt_end; kt = __builtin_amdgcn_readfirstlane(kt + 1)) {
+      tile(yes{}, par_rt{}, kt);
+    }
   }
 
   if (qrow < n) {
@@ -487,10 +529,11 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
-  using T = QTile<D>;
+  constexpr int NW = (D == 128) ? 8 : 4;
+  using T = QTile<D, NW>;
   const int n_qt = (a.n + T::BRQ - 1) / T::BRQ;
   const int total = (int)(a.bh * n_qt);
-  return launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3(total), dim3(256), s,
+  return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL>, dim3(total), dim3(NW * 64), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
