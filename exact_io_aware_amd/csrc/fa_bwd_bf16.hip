@@ -147,9 +147,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using T = KVTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int kw = w & 3;   // key block of this wave
@@ -173,16 +172,36 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   const int n_qt = (n + T::BRQ - 1) / T::BRQ;
   const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
+  // DMA sources of the Q / dO tiles: lane `lane` fills bytes 16*lane of
+  // 1-KB block w + NW*i, i.e. row o / ROW, physical chunk (o % ROW) / 16 =
+  // logical chunk ^ swizzle; element offsets from the tile's first row.
+  int goff[T::T_BLK];
+#pragma unroll
+  for (int i = 0; i < T::T_BLK; ++i) {
+    const int o = (w + T::NW * i) * 1024 + lane * 16;
+    const int row = o / T::ROW;
+    goff[i] = row * D + ((((o % T::ROW) >> 4) ^ tile_swz<D>(row)) * 8);
+  }
   // Stage fill: Q and dO tiles (1-KB blocks split over the waves) and the
   // per-row lse2 and D (one 256-B block per 64 rows, clamped rows; rows past
   // the end are masked in the math).
   auto issue_stage = [&](int qt, int stage) {
     unsigned char* st = smem + T::OFF_ST + stage * T::STAGE;
     const int q0 = qt * T::BRQ;
+    if (q0 + T::BRQ <= n) {
+      const bf16* qb = Q + hoff + (int64_t)q0 * D;
+      const bf16* db = dO + hoff + (int64_t)q0 * D;
 #pragma unroll
-    for (int i = 0; i < T::T_BLK; ++i) {
-      dma_tile_block<D>(Q + hoff, q0, n, st, w + T::NW * i, lane);
-      dma_tile_block<D>(dO + hoff, q0, n, st + T::S_DO, w + T::NW * i, lane);
+      for (int i = 0; i < T::T_BLK; ++i) {
+        dma16(qb + (uint32_t)goff[i], st + (w + T::NW * i) * 1024);
+        dma16(db + (uint32_t)goff[i], st + T::S_DO + (w + T::NW * i) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::T_BLK; ++i) {
+        dma_tile_block<D>(Q + hoff, q0, n, st, w + T::NW * i, lane);
+        dma_tile_block<D>(dO + hoff, q0, n, st + T::S_DO, w + T::NW * i, lane);
+      }
     }
     constexpr int RB = T::BRQ / 64;  // 256-B row blocks per statistic
     if (w < 2 * RB) {
@@ -207,9 +226,16 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const unsigned char* sk = smem + kw * 32 * T::ROW;
   const unsigned char* sv = smem + T::OFF_V + kw * 32 * T::ROW;
 
-  int stage = 0;
-  if (qt_begin < n_qt) issue_stage(qt_begin, 0);
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
+  // One query tile: wait for it (loaded one tile ahead) and let every wave
+  // finish the previous one, load the next tile into the freed stage, then
+  // accumulate this wave's query blocks.  MASK: the tile has queries before
+  // some of this wave's keys (causal) or past the end; fully masked blocks
+  // are skipped.  PAR is the stage parity when known at compile time (every
+  // LDS address is then a register plus an immediate), else -1.
+  auto tile = [&](auto mask_tag, auto par_tag, int qt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    const int stage = (PAR >= 0) ? PAR : ((qt - qt_begin) & 1);
     wait_dma();
     __syncthreads();
     if (qt + 1 < n_qt) issue_stage(qt + 1, stage ^ 1);
@@ -220,7 +246,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int qi = 0; qi < T::QBW; ++qi) {
       const int qb = qh * T::QBW + qi;
       const int qq0 = qt * T::BRQ + qb * 32;
-      if (CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
+      if (MASK && CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
       // S = Q K^T and dP = dO V^T (M = query, N = key), both operands from LDS.
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -231,8 +257,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
       }
-      // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.
-      const bool need_mask = (CAUSAL && qq0 < kw0 + 31) || (qq0 + 31 >= n);
+      // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.  With MASK, P is
+      // zero for queries before this lane's key or past the end: qrel is the
+      // first visible query relative to qq0 + h*4, qend the end.
+      const int qlo = (CAUSAL ? key : 0) - qq0 - h * 4;
+      const int qhi = n - qq0 - h * 4;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 L = *reinterpret_cast<const f32x4*>(sL + qb * 32 + g * 8 + h * 4);
@@ -241,9 +270,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
           float p = fast_exp2(fmaf(s[i], c_log2, -L[t]));
-          if (need_mask) {
-            const int q = qq0 + g * 8 + h * 4 + t;
-            if ((CAUSAL && q < key) || q >= n) p = 0.f;
+          if constexpr (MASK) {
+            const int qr = g * 8 + t;
+            if (qr < qlo || qr >= qhi) p = 0.f;
           }
           s[i] = p;
           dp[i] = p * (dp[i] - Dv[t]);
@@ -267,7 +296,40 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
       }
     }
-    stage ^= 1;
+  };
+
+  using yes = std::true_type;
+  using no = std::false_type;
+  using par0 = std::integral_constant<int, 0>;
+  using par1 = std::integral_constant<int, 1>;
+  using par_rt = std::integral_constant<int, -1>;
+  if (qt_begin < n_qt) {
+    issue_stage(qt_begin, 0);
+    // Masked tiles: under the causal rule those holding the first 128
+    // queries (they meet the diagonal of the workgroup's keys), and the
+    // tile reaching past the end.  Unmasked tiles run in pairs with static
+    // stage parity (stage = (qt - qt_begin) & 1).
+    const int head_end = min(n_qt, qt_begin + (CAUSAL ? T::BCK / T::BRQ : 0));
+    const int full_end = n / T::BRQ;  // tiles before this are fully in range
+    int qt = qt_begin;
+#pragma unroll 1
+    for (; qt < head_end; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
+      tile(yes{}, par_rt{}, qt);
+    }
+    if (((qt - qt_begin) & 1) && qt < full_end) {
+      tile(no{}, par1{}, qt);
+      qt = __builtin_amdgcn_readfirstlane(qt + 1);
+    }
+#pragma unroll 1
+    while (qt + 1 < full_end) {
+      tile(no{}, par0{}, qt);
+      tile(no{}, par1{}, qt + 1);
+      qt = __builtin_amdgcn_readfirstlane(qt + 2);
+    }
+#pragma unroll 1
+    for (; qt < n_qt; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
+      tile(yes{}, par_rt{}, qt);
+    }
   }
 
   // Add the two query halves' partial sums through LDS, then store once.
