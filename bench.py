@@ -151,26 +151,23 @@ def time_workload(name, steps, warmup, calib_mb=0):
                 alg=alg)
 
 
-def time_forward_only(name, steps, warmup):
-    """Per-workload forward timing (used by --all)."""
+def time_passes(name, steps, warmup):
+    """Per-workload timing of every pass the workload lists (used by --all):
+    the forward, and for workloads with a backward the whole fa_bwd (or
+    fa_bwd_blocksparse) call, inputs O and LSE from the forward (untimed)."""
     import torch
 
     from exact_io_aware_amd import fa, workloads
 
     w = workloads.workload(name)
     dev = torch.device("cuda:0")
-    x = workloads.workload_inputs(name, with_do=False, device=dev)
+    x = workloads.workload_inputs(name, with_do="bwd" in w["passes"],
+                                  device=dev)
     mask = workloads.workload_mask(w)
     mask_t = torch.from_numpy(mask).to(dev) if mask is not None else None
     out = []
-    for causal in w["causal"]:
-        def run():
-            if mask_t is not None:
-                fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], mask_t,
-                                      scale=w["scale"], causal=causal)
-            else:
-                fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"],
-                          causal=causal)
+
+    def median_ms(run):
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
@@ -183,15 +180,43 @@ def time_forward_only(name, steps, warmup):
             b.record()
             times.append((a, b))
         torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+        return sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+
+    for causal in w["causal"]:
+        def fwd():
+            if mask_t is not None:
+                return fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], mask_t,
+                                             scale=w["scale"], causal=causal)
+            return fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"],
+                             causal=causal)
         if mask is not None:
             flops = 4.0 * w["d"] * 128 * 128 * float(mask.sum()) * w["B"] * w["H"]
         else:
             flops = fwd_flops(w["B"], w["H"], w["N"], w["d"], causal)
-        tf = flops / (ms * 1e-3) / 1e12
         peak = PEAK_F32_TFLOPS if w["dtype"] == "f32" else PEAK_BF16_TFLOPS
-        out.append(dict(workload=name, causal=causal, pass_="fwd",
-                        ms_median=ms, tflops=tf, frac_peak=tf / peak))
+        passes = [("fwd", fwd, flops)]
+        if "bwd" in w["passes"]:
+            o, lse = fwd()
+            ws = torch.empty(fa.fa_bwd_workspace_bytes(w["B"], w["H"], w["N"],
+                                                       w["d"]),
+                             dtype=torch.uint8, device=dev)
+            grads = [torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
+                     for _ in range(3)]
+
+            def bwd():
+                kw = dict(scale=w["scale"], causal=causal, workspace=ws,
+                          dq=grads[0], dk=grads[1], dv=grads[2])
+                if mask_t is not None:
+                    fa.fa_bwd_blocksparse(x["q"], x["k"], x["v"], o, x["do"],
+                                          lse, mask_t, **kw)
+                else:
+                    fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, **kw)
+            passes.append(("bwd", bwd, 2.5 * flops))
+        for pname, run, fl in passes:
+            ms = median_ms(run)
+            tf = fl / (ms * 1e-3) / 1e12
+            out.append(dict(workload=name, causal=causal, pass_=pname,
+                            ms_median=ms, tflops=tf, frac_peak=tf / peak))
     return out
 
 
@@ -313,7 +338,7 @@ def main():
     if args.all:
         from exact_io_aware_amd import workloads
         for name in workloads.WORKLOADS:
-            for res in time_forward_only(name, max(args.steps, 20), 3):
+            for res in time_passes(name, max(args.steps, 20), 3):
                 print(json.dumps(res), flush=True)
     print(json.dumps(line), flush=True)
 

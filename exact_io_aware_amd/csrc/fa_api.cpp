@@ -106,11 +106,19 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
                      const void* workspace, size_t workspace_bytes, int64_t B,
                      int64_t H, int64_t N, int64_t d, fa_dtype dt, float scale,
                      bool check_scale, int causal, fa::BwdArgs* out,
-                     bool* empty) {
+                     bool* empty, const uint8_t* mask = nullptr,
+                     int64_t block_m = 128, int64_t block_n = 128,
+                     bool sparse_call = false) {
   int64_t bh = 0;
   fa_status st = check_shape(B, H, N, d, dt, empty, &bh);
   if (st != FA_OK) return st;
   if (check_scale && !scale_ok(scale)) return FA_ERR_ARG;
+  if (sparse_call) {
+    if (block_m <= 0 || block_n <= 0 || block_m % 128 != 0 ||
+        block_n % 128 != 0 || block_m > kMaxN || block_n > kMaxN) {
+      return FA_ERR_MASK;
+    }
+  }
   if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (*empty) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
@@ -141,6 +149,10 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
+  a.mask = sparse_call ? mask : nullptr;
+  a.block_m = (int)(sparse_call ? block_m : 128);
+  a.block_n = (int)(sparse_call ? block_n : 128);
+  a.mask_cols = (int)((N + a.block_n - 1) / a.block_n);
   *out = a;
   return FA_OK;
 }
@@ -226,6 +238,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
                             workspace, workspace_bytes, B, H, N, d, dt, scale,
                             true, causal, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(fa::launch_bwd_preprocess(a, s));
+  if (st != FA_OK) return st;
+  st = from_hip(fa::launch_bwd_dkdv(a, s));
+  if (st != FA_OK) return st;
+  return from_hip(fa::launch_bwd_dq(a, s));
+}
+
+fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty, mask, block_m, block_n,
+                            true);
   if (st != FA_OK || empty) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = from_hip(fa::launch_bwd_preprocess(a, s));

@@ -136,14 +136,15 @@ __device__ __forceinline__ void tr_offsets(int lane, int toff[DB][2]) {
 // operands), which keeps the per-wave register footprint within the 256
 // registers that two waves per SIMD allow.  Query tiles are double-buffered
 // and filled by direct global-to-LDS loads.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ ws_d,
                      const float* __restrict__ ws_lse2, float* __restrict__ dK,
                      float* __restrict__ dV, int n, int n_ktiles, int total,
-                     float c_log2, float scale) {
+                     float c_log2, float scale, const uint8_t* __restrict__ mask,
+                     int mask_cols, int block_m, int block_n) {
   using T = KVTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
 
@@ -226,19 +227,30 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const unsigned char* sk = smem + kw * 32 * T::ROW;
   const unsigned char* sv = smem + T::OFF_V + kw * 32 * T::ROW;
 
+  // Block-sparse: the query tiles whose mask block in this workgroup's key
+  // column is nonzero (a 64-row tile lies in one 128-multiple block row).
+  const uint8_t* mcol = SPARSE ? mask + k0 / block_n : nullptr;
+  auto next_on = [&](int qt) -> int {
+    ++qt;
+    if constexpr (SPARSE) {
+      while (qt < n_qt && mcol[(int64_t)((qt * T::BRQ) / block_m) * mask_cols] == 0) ++qt;
+    }
+    return __builtin_amdgcn_readfirstlane(qt);
+  };
   // One query tile: wait for it (loaded one tile ahead) and let every wave
   // finish the previous one, load the next tile into the freed stage, then
   // accumulate this wave's query blocks.  MASK: the tile has queries before
   // some of this wave's keys (causal) or past the end; fully masked blocks
   // are skipped.  PAR is the stage parity when known at compile time (every
-  // LDS address is then a register plus an immediate), else -1.
-  auto tile = [&](auto mask_tag, auto par_tag, int qt) {
+  // LDS address is then a register plus an immediate), else -1 (then
+  // `stage`).  `qt_next` is the tile that follows.
+  auto tile = [&](auto mask_tag, auto par_tag, int qt, int stage_rt, int qt_next) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
-    const int stage = (PAR >= 0) ? PAR : ((qt - qt_begin) & 1);
+    const int stage = (PAR >= 0) ? PAR : stage_rt;
     wait_dma();
     __syncthreads();
-    if (qt + 1 < n_qt) issue_stage(qt + 1, stage ^ 1);
+    if (qt_next < n_qt) issue_stage(qt_next, stage ^ 1);
     const unsigned char* st = smem + T::OFF_ST + stage * T::STAGE;
     const float* sL = reinterpret_cast<const float*>(st + T::S_L);
     const float* sD = reinterpret_cast<const float*>(st + T::S_D);
@@ -303,7 +315,20 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using par0 = std::integral_constant<int, 0>;
   using par1 = std::integral_constant<int, 1>;
   using par_rt = std::integral_constant<int, -1>;
-  if (qt_begin < n_qt) {
+  if constexpr (SPARSE) {
+    // Visited tiles in order, each in the masked form; the stage parity
+    // alternates over visited tiles.
+    int qt = next_on(qt_begin - 1);
+    if (qt < n_qt) issue_stage(qt, 0);
+    int stage = 0;
+#pragma unroll 1
+    while (qt < n_qt) {
+      const int qn = next_on(qt);
+      tile(yes{}, par_rt{}, qt, stage, qn);
+      qt = qn;
+      stage ^= 1;
+    }
+  } else if (qt_begin < n_qt) {
     issue_stage(qt_begin, 0);
     // Masked tiles: under the causal rule those holding the first 128
     // queries (they meet the diagonal of the workgroup's keys), and the
@@ -314,21 +339,21 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     int qt = qt_begin;
 #pragma unroll 1
     for (; qt < head_end; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
-      tile(yes{}, par_rt{}, qt);
+      tile(yes{}, par_rt{}, qt, (qt - qt_begin) & 1, qt + 1);
     }
     if (((qt - qt_begin) & 1) && qt < full_end) {
-      tile(no{}, par1{}, qt);
+      tile(no{}, par1{}, qt, 1, qt + 1);
       qt = __builtin_amdgcn_readfirstlane(qt + 1);
     }
 #pragma unroll 1
     while (qt + 1 < full_end) {
-      tile(no{}, par0{}, qt);
-      tile(no{}, par1{}, qt + 1);
+      tile(no{}, par0{}, qt, 0, qt + 1);
+      tile(no{}, par1{}, qt + 1, 1, qt + 2);
       qt = __builtin_amdgcn_readfirstlane(qt + 2);
     }
 #pragma unroll 1
     for (; qt < n_qt; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
-      tile(yes{}, par_rt{}, qt);
+      tile(yes{}, par_rt{}, qt, (qt - qt_begin) & 1, qt + 1);
     }
   }
 
@@ -396,13 +421,15 @@ struct QTile {
 // has 4 waves and two run per CU.  Wave w owns queries q0 + 32w .. + 31; Q
 // and dO stay in registers as B operands.  K/V tiles are double-buffered
 // and filled by direct global-to-LDS loads one tile ahead.
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ ws_d,
                    const float* __restrict__ ws_lse2, float* __restrict__ dQ,
-                   int n, int n_qtiles, int total, float c_log2, float scale) {
+                   int n, int n_qtiles, int total, float c_log2, float scale,
+                   const uint8_t* __restrict__ mask, int mask_cols, int block_m,
+                   int block_n) {
   using T = QTile<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
 
@@ -482,13 +509,25 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // finish the previous one, load the next tile into the freed stage, then
   // accumulate dQ^T.  PAR is the stage parity when known at compile time
   // (every LDS address is then a register plus an immediate), else -1.
-  auto tile = [&](auto mask_tag, auto par_tag, int kt) {
+  // Block-sparse: the key tiles whose mask block in this workgroup's row is
+  // nonzero (a workgroup's 128 rows lie in one block row, a key tile in one
+  // block column).
+  const uint8_t* mrow =
+      SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
+  auto next_on = [&](int kt) -> int {
+    ++kt;
+    if constexpr (SPARSE) {
+      while (kt < kt_end && mrow[(kt * T::BCK) / block_n] == 0) ++kt;
+    }
+    return __builtin_amdgcn_readfirstlane(kt);
+  };
+  auto tile = [&](auto mask_tag, auto par_tag, int kt, int stage_rt, int kt_next) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
-    const int stage = (PAR >= 0) ? PAR : (kt & 1);
+    const int stage = (PAR >= 0) ? PAR : stage_rt;
     wait_dma();
     __syncthreads();
-    if (kt + 1 < kt_end) fill(kt + 1, stage ^ 1);
+    if (kt_next < kt_end) fill(kt_next, stage ^ 1);
     const unsigned char* st = smem + stage * T::STAGE;
     const int kbase = kt * T::BCK;
     // Last visible key of this lane's row relative to the key in register 0
@@ -534,22 +573,35 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using par0 = std::integral_constant<int, 0>;
   using par1 = std::integral_constant<int, 1>;
   using par_rt = std::integral_constant<int, -1>;
-  if (kt_end > 0) {
+  if constexpr (SPARSE) {
+    // Visited tiles in order, each in the masked form; the stage parity
+    // alternates over visited tiles.
+    int kt = next_on(-1);
+    if (kt < kt_end) fill(kt, 0);
+    int stage = 0;
+#pragma unroll 1
+    while (kt < kt_end) {
+      const int kn = next_on(kt);
+      tile(yes{}, par_rt{}, kt, stage, kn);
+      kt = kn;
+      stage ^= 1;
+    }
+  } else if (kt_end > 0) {
     fill(0, 0);
     // Tiles needing the element mask come last; unmasked tiles run in
     // pairs with static stage parity.
     int kt = 0;
 #pragma unroll 1
     while (kt + 1 < kt_end && !needs_mask(kt + 1)) {
-      tile(no{}, par0{}, kt);
-      tile(no{}, par1{}, kt + 1);
+      tile(no{}, par0{}, kt, 0, kt + 1);
+      tile(no{}, par1{}, kt + 1, 1, kt + 2);
       kt = __builtin_amdgcn_readfirstlane(kt + 2);
     }
     // (At most one unmasked tile remains here; it takes the masked form,
     // whose mask is then a no-op.)
 #pragma unroll 1
     for (; kt < kt_end; kt = __builtin_amdgcn_readfirstlane(kt + 1)) {
-      tile(yes{}, par_rt{}, kt);
+      tile(yes{}, par_rt{}, kt, kt & 1, kt + 1);
     }
   }
 
@@ -577,29 +629,42 @@ hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
                        a.ws_lse2, rows);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = KVTile<D>;
   const int n_kt = (a.n + T::BCK - 1) / T::BCK;
   const int total = (int)(a.bh * n_kt);
-  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3(total), dim3(512), s,
+  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SPARSE>, dim3(total), dim3(512), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
-                       a.scale * kLog2e, a.scale);
+                       a.scale * kLog2e, a.scale, a.mask, a.mask_cols, a.block_m,
+                       a.block_n);
 }
 
-template <int D, bool CAUSAL>
+// d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
+// rows so that a workgroup lies in one 128-multiple block row of the mask.
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
-  constexpr int NW = (D == 128) ? 8 : 4;
+  constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = QTile<D, NW>;
   const int n_qt = (a.n + T::BRQ - 1) / T::BRQ;
   const int total = (int)(a.bh * n_qt);
-  return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL>, dim3(total), dim3(NW * 64), s,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
-                       (const bf16*)a.dout, (const float*)a.ws_d,
+  return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
+                       dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
-                       a.scale * kLog2e, a.scale);
+                       a.scale * kLog2e, a.scale, a.mask, a.mask_cols, a.block_m,
+                       a.block_n);
+}
+
+template <int D, bool SPARSE>
+hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
+  return a.causal ? dkdv_t<D, true, SPARSE>(a, s) : dkdv_t<D, false, SPARSE>(a, s);
+}
+template <int D, bool SPARSE>
+hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
+  return a.causal ? dq_t<D, true, SPARSE>(a, s) : dq_t<D, false, SPARSE>(a, s);
 }
 
 }  // namespace
@@ -609,13 +674,13 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 128) return a.causal ? dkdv_t<128, true>(a, s) : dkdv_t<128, false>(a, s);
-  return a.causal ? dkdv_t<64, true>(a, s) : dkdv_t<64, false>(a, s);
+  if (a.mask) return a.d == 128 ? dkdv_c<128, true>(a, s) : dkdv_c<64, true>(a, s);
+  return a.d == 128 ? dkdv_c<128, false>(a, s) : dkdv_c<64, false>(a, s);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.d == 128) return a.causal ? dq_t<128, true>(a, s) : dq_t<128, false>(a, s);
-  return a.causal ? dq_t<64, true>(a, s) : dq_t<64, false>(a, s);
+  if (a.mask) return a.d == 128 ? dq_c<128, true>(a, s) : dq_c<64, true>(a, s);
+  return a.d == 128 ? dq_c<128, false>(a, s) : dq_c<64, false>(a, s);
 }
 
 }  // namespace fa

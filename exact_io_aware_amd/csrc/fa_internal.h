@@ -42,6 +42,10 @@ struct BwdArgs {
   int d;
   float scale;
   int causal;
+  const uint8_t* mask;     // nullptr = dense
+  int mask_cols;           // ceil(n / block_n)
+  int block_m;             // multiple of 128
+  int block_n;             // multiple of 128
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

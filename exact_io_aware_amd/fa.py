@@ -16,7 +16,8 @@ import torch
 from . import _build
 
 __all__ = [
-    "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_preprocess",
+    "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse",
+    "fa_bwd_preprocess",
     "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
     "fa_version", "library", "LIB_PATH",
 ]
@@ -54,6 +55,8 @@ def library():
                                I64, I64, P],
         "fa_bwd": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F,
                    I, P],
+        "fa_bwd_blocksparse": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
+                               I64, I, F, I, P, I64, I64, P],
         "fa_bwd_preprocess": [P, P, P, P, SZ, I64, I64, I64, I64, I, P],
         "fa_bwd_dkdv": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I,
                         P],
@@ -136,6 +139,20 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     return o, lse_t
 
 
+def _mask_arg(block_mask, N, block_m, block_n, device):
+    """The block mask as a contiguous uint8 device tensor (or None)."""
+    if block_mask is None:
+        return None
+    rows = -(-N // int(block_m))
+    cols = -(-N // int(block_n))
+    if tuple(block_mask.shape) != (rows, cols):
+        raise ValueError(f"block mask must be {rows} x {cols}, got "
+                         f"{tuple(block_mask.shape)}")
+    if block_mask.device != device:
+        raise ValueError("block mask must be on the inputs' device")
+    return block_mask.to(torch.uint8).contiguous()
+
+
 def fa_fwd_blocksparse(q, k, v, block_mask, block_m=128, block_n=128,
                        scale=None, causal=False, out=None, lse=None):
     """Forward over the nonzero blocks of ``block_mask`` only.
@@ -146,16 +163,7 @@ def fa_fwd_blocksparse(q, k, v, block_mask, block_m=128, block_n=128,
     """
     B, H, N, d = _shape4(q, k, v)
     lib = library()
-    mask_t = None
-    if block_mask is not None:
-        rows = -(-N // int(block_m))
-        cols = -(-N // int(block_n))
-        if tuple(block_mask.shape) != (rows, cols):
-            raise ValueError(f"block mask must be {rows} x {cols}, got "
-                             f"{tuple(block_mask.shape)}")
-        if block_mask.device != q.device:
-            raise ValueError("block mask must be on the inputs' device")
-        mask_t = block_mask.to(torch.uint8).contiguous()
+    mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
     o = torch.empty_like(q) if out is None else out
     lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=q.device)
              if lse is None else lse)
@@ -194,6 +202,27 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
                           ws_bytes, B, H, N, d, _dtype_code(q),
                           _scale(scale, d), int(bool(causal)),
                           _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, block_m=128,
+                       block_n=128, scale=None, causal=False, workspace=None,
+                       dq=None, dk=None, dv=None):
+    """Gradients of ``fa_fwd_blocksparse`` (same mask; o, lse from it)."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    lib = library()
+    mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(q.shape, **f32) if dk is None else dk
+    dv = torch.empty(q.shape, **f32) if dv is None else dv
+    ws, ws_bytes = _workspace(B, H, N, d, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_blocksparse(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, B, H, N, d, _dtype_code(q),
+            _scale(scale, d), int(bool(causal)), _ptr(mask_t), int(block_m),
+            int(block_n), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -52,7 +52,7 @@ WORKLOADS = {
     "bwd_4x16x4096x128": _w("bwd_4x16x4096x128", 4, 16, 4096, 128, "bf16",
                             (True,), ("fwd", "bwd"), seed=4),
     "sparse_1x16x16384x64": _w("sparse_1x16x16384x64", 1, 16, 16384, 64,
-                               "bf16", (False,), ("fwd",), seed=5,
+                               "bf16", (False,), ("fwd", "bwd"), seed=5,
                                sparse=dict(block=128, frac=0.25, seed=5)),
 }
 

@@ -135,7 +135,30 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
                  float scale, int causal, void* stream);
 
-/* Bytes of workspace fa_bwd needs (0 for empty problems). */
+/*
+ * fa_bwd_blocksparse — backward pass of fa_fwd_blocksparse: the exact
+ * gradient of that forward ([XYZ] section "Block-Sparse FlashAttention": the
+ * backward visits the same nonzero blocks as the forward), by recomputation
+ * as fa_bwd.  Query/key tiles whose mask block is 0 are skipped in both
+ * gradient passes; a query that sees no key gets dQ = 0 and a key no query
+ * sees gets dK = dV = 0.
+ *
+ * mask, block_m, block_n : as fa_fwd_blocksparse (mask == NULL means every
+ *                          block is on: identical to fa_bwd).
+ * o, lse                 : from fa_fwd_blocksparse with the same mask.
+ * Other arguments, workspace and outputs as fa_bwd.  FA_ERR_MASK for invalid
+ * block sizes.
+ */
+fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, void* stream);
+
+/* Bytes of workspace fa_bwd and fa_bwd_blocksparse need (0 for empty
+ * problems). */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*

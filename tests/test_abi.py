@@ -161,3 +161,28 @@ def test_binding_fails_loudly_without_gpu_tensors(lib):
     q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)  # CPU tensors are rejected, never computed on CPU
+
+
+def bwd_sparse(lib, mask=P, bm=128, bn=128, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, B=1,
+             H=2, N=384, d=64, dt=BF16, scale=0.125, causal=0)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    return lib.fa_bwd_blocksparse(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+        a["dv"], a["ws"], ws_bytes, a["B"], a["H"], a["N"], a["d"], a["dt"],
+        a["scale"], a["causal"], mask, bm, bn, None)
+
+
+def test_bwd_blocksparse_validation(lib):
+    assert bwd_sparse(lib, bm=64) == FA_ERR_MASK
+    assert bwd_sparse(lib, bn=200) == FA_ERR_MASK
+    assert bwd_sparse(lib, bm=-128) == FA_ERR_MASK
+    assert bwd_sparse(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    assert bwd_sparse(lib, scale=0.0) == FA_ERR_ARG
+    assert bwd_sparse(lib, ws_bytes=16) == FA_ERR_ARG
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert bwd_sparse(lib, **{name: None}) == FA_ERR_NULL, name
+    assert bwd_sparse(lib, dk=MISALIGNED) == FA_ERR_ALIGN
+    assert bwd_sparse(lib, N=0, q=None, ws=None) == FA_OK
