@@ -50,6 +50,7 @@ __all__ = [
     "tiled_fwd_fa1_head",
     "causal_tiles_visited",
     "expand_block_mask",
+    "attention_decode_head",
 ]
 
 NEG_INF = -np.inf
@@ -64,11 +65,14 @@ def _f64(x):
 # ---------------------------------------------------------------------------
 
 def visible(rows, n_keys, causal=False, block_mask=None, block_m=128,
-            block_n=128):
+            block_n=128, q_pos0=0):
     """Boolean matrix vis[r, j]: key j is visible to query rows[r].
 
     Causal rule: j <= i ([REAPER], causal-mask question of the chapter
-    summary: query block i needs only key blocks j <= i; read element-wise).
+    summary: query block i needs only key blocks j <= i; read element-wise),
+    where i = q_pos0 + row is the query's position in the key sequence
+    (q_pos0 = 0 when queries and keys are the same tokens; a decoding step's
+    Nq new queries are the last Nq positions, q_pos0 = Nk - Nq).
     Block-sparse rule: the entry of the block mask covering (i, j) is nonzero
     ([XYZ], section "Block-Sparse FlashAttention").  Both apply by AND.
     """
@@ -76,7 +80,7 @@ def visible(rows, n_keys, causal=False, block_mask=None, block_m=128,
     cols = np.arange(n_keys, dtype=np.int64)
     vis = np.ones((rows.size, n_keys), dtype=bool)
     if causal:
-        vis &= cols[None, :] <= rows[:, None]
+        vis &= cols[None, :] <= q_pos0 + rows[:, None]
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         vis &= bm[rows[:, None] // block_m, cols[None, :] // block_n]
@@ -135,6 +139,28 @@ def attention_fwd_head(q, k, v, scale, causal=False, block_mask=None,
         with np.errstate(divide="ignore"):
             LSE[c0:c0 + r.size] = np.where(np.isneginf(m), NEG_INF,
                                            m + np.log(l))
+    return O, LSE
+
+
+def attention_decode_head(q, k, v, scale, causal=False):
+    """O and LSE of one head for Nq queries against Nk >= Nq keys, the
+    queries being the last Nq tokens of the sequence ([REAPER] 3.6: in
+    decoding Q is one token, or a few, while K and V span the whole context).
+    The definition is that of ``attention_fwd_head``; under the causal rule
+    query row r sits at position Nk - Nq + r."""
+    q, k = _f64(q), _f64(k)
+    n_q, n_k = q.shape[0], k.shape[0]
+    assert n_k >= n_q, "decoding queries are the last Nq of the Nk tokens"
+    v = _f64(v)
+    O = np.zeros((n_q, v.shape[1]))
+    LSE = np.full(n_q, NEG_INF)
+    r = np.arange(n_q)
+    S = scale * (q @ k.T)
+    S = np.where(visible(r, n_k, causal, q_pos0=n_k - n_q), S, NEG_INF)
+    P, m, l = _softmax_rows(S)
+    O[:] = P @ v
+    with np.errstate(divide="ignore"):
+        LSE[:] = np.where(np.isneginf(m), NEG_INF, m + np.log(l))
     return O, LSE
 
 

@@ -433,6 +433,43 @@ def check_block_sparse(orc):
                     _close(dv, Tdv, 1e-12, f"mask {bits} dV")
 
 
+def check_decode(orc):
+    """Decoding (Nq queries = the last Nq of Nk tokens, [REAPER] 3.6):
+    with Nq = Nk it is the square problem; its rows equal the last Nq rows of
+    the square causal problem over the same tokens; a single causal query
+    sees every key; and it agrees with PyTorch's float64 attention under the
+    explicit bottom-right mask (key j visible to row r iff j <= Nk - Nq + r,
+    built here with Python loops)."""
+    r = _rng(40)
+    d = 5
+    for n_k in (1, 6, 13):
+        k, v = r.standard_normal((n_k, d)), r.standard_normal((n_k, 3))
+        q_all = r.standard_normal((n_k, d))
+        for causal in (False, True):
+            O_sq, l_sq = orc.attention_fwd_head(q_all, k, v, 0.6, causal)
+            O_d, l_d = orc.attention_decode_head(q_all, k, v, 0.6, causal)
+            _close(O_d, O_sq, 0.0, "decode Nq = Nk O")
+            _close(l_d, l_sq, 0.0, "decode Nq = Nk LSE")
+            for n_q in range(1, n_k + 1):
+                q = q_all[n_k - n_q:]
+                O, l = orc.attention_decode_head(q, k, v, 0.6, causal)
+                _close(O, O_sq[n_k - n_q:], EXACT_TOL, "decode = last rows O")
+                _close(l, l_sq[n_k - n_q:], EXACT_TOL, "decode = last rows LSE")
+        O1, l1 = orc.attention_decode_head(q_all[-1:], k, v, 0.6, True)
+        O0, l0 = orc.attention_decode_head(q_all[-1:], k, v, 0.6, False)
+        _close(O1, O0, 0.0, "one causal query sees every key")
+        _close(l1, l0, 0.0, "one causal query LSE")
+    n_q, n_k = 3, 8
+    q, k = r.standard_normal((n_q, d)), r.standard_normal((n_k, d))
+    v, do = r.standard_normal((n_k, 4)), r.standard_normal((n_q, 4))
+    elem = np.array([[j <= n_k - n_q + i for j in range(n_k)]
+                     for i in range(n_q)])
+    To, Tl, _, _, _ = _torch_reference(q, k, v, do, 0.45, False, elem)
+    O, lse = orc.attention_decode_head(q, k, v, 0.45, True)
+    _close(O, To, 1e-12, "decode vs torch O")
+    _close(lse, Tl, 1e-12, "decode vs torch LSE")
+
+
 ALL_CHECKS = [
     check_fig1_divide_last,
     check_fig2_streamed_pairs,
@@ -449,4 +486,5 @@ ALL_CHECKS = [
     check_tile_invariance,
     check_causal_tile_count,
     check_block_sparse,
+    check_decode,
 ]

@@ -25,10 +25,14 @@ MUTATIONS = [
      "S = (q[r] @ k.T)", 1),
     ("fwd: P transposed in O = P V", "O[c0:c0 + r.size] = P @ v",
      "O[c0:c0 + r.size] = P.T @ v", 0),
-    ("causal: strict inequality", "cols[None, :] <= rows[:, None]",
-     "cols[None, :] < rows[:, None]", 0),
-    ("causal: reversed", "cols[None, :] <= rows[:, None]",
-     "cols[None, :] >= rows[:, None]", 0),
+    ("causal: strict inequality", "cols[None, :] <= q_pos0 + rows[:, None]",
+     "cols[None, :] < q_pos0 + rows[:, None]", 0),
+    ("causal: reversed", "cols[None, :] <= q_pos0 + rows[:, None]",
+     "cols[None, :] >= q_pos0 + rows[:, None]", 0),
+    ("causal: query offset subtracted",
+     "cols[None, :] <= q_pos0 + rows[:, None]",
+     "cols[None, :] <= rows[:, None] - q_pos0", 0),
+    ("decode: offset from the wrong end", "q_pos0=n_k - n_q", "q_pos0=0", 0),
     ("block mask: indices swapped",
      "bm[rows[:, None] // block_m, cols[None, :] // block_n]",
      "bm[cols[None, :] // block_n, rows[:, None] // block_m]", 0),
