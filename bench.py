@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4096 x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 METRIC = "attention fwd/bwd TFLOP/s (bf16, N=8192 d=128 causal) + % MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -51,6 +52,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fa_fwd_bf16.hip"],
     "bwd_dkdv_kernel": ["fa_bwd_bf16.hip"],
     "bwd_dq_kernel": ["fa_bwd_bf16.hip"],
+    "splitkv_bf16_kernel": ["fa_fwd_bf16.hip"],
 }
 
 
@@ -220,6 +222,52 @@ def time_passes(name, steps, warmup):
     return out
 
 
+def time_decode(name, steps, warmup):
+    """Timing of the split-KV forward on a decoding workload (used by --all):
+    the whole fa_fwd_splitkv call (chunk pass + merge), median over steps.
+    The work is a matrix-vector product per head, bound by HBM bandwidth, so
+    the figure is algorithmic bytes (Q, K, V read once; O and LSE written
+    once) over the median time, against the 8 TB/s HBM peak."""
+    import torch
+
+    from exact_io_aware_amd import fa, workloads
+
+    w = workloads.workload(name)
+    B, H, Nq, Nk, d = w["B"], w["H"], w["Nq"], w["Nk"], w["d"]
+    dev = torch.device("cuda:0")
+    x = workloads.make_decode_inputs(B, H, Nq, Nk, d, w["seed"], w["sigma"],
+                                     device=dev)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    out = []
+    for causal in w["causal"]:
+        def run():
+            fa.fa_fwd_splitkv(x["q"], x["k"], x["v"], scale=w["scale"],
+                              causal=causal, workspace=ws, out=o, lse=lse)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            times.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+        nbytes = B * H * (2 * Nq * d + 2 * 2 * Nk * d + 4 * Nq)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append(dict(workload=name, causal=causal, pass_="decode",
+                        ms_median=ms, gbytes_per_s=gbs,
+                        frac_hbm_peak=gbs / PEAK_HBM_GBS,
+                        chunks=fa.fa_fwd_splitkv_chunks(B, H, Nq, Nk, d, 0)))
+    return out
+
+
 def cpu_baseline(name, budget_s=12.0, max_heads=8):
     """The fp64 oracle (forward + backward of whole heads) on host cores."""
     import numpy as np
@@ -339,6 +387,9 @@ def main():
         from exact_io_aware_amd import workloads
         for name in workloads.WORKLOADS:
             for res in time_passes(name, max(args.steps, 20), 3):
+                print(json.dumps(res), flush=True)
+        for name in workloads.DECODE_WORKLOADS:
+            for res in time_decode(name, max(args.steps, 20), 3):
                 print(json.dumps(res), flush=True)
     print(json.dumps(line), flush=True)
 

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <limits>
 
 #include "../../include/fa.h"
@@ -157,9 +158,110 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
   return FA_OK;
 }
 
+// Chunk plan of the split-KV forward.  requested > 0 caps the chunk count;
+// 0 picks enough chunks for about 2048 workgroups (eight per CU) with at
+// least 8 key tiles (256 keys) per chunk.  The tiles are then spread evenly
+// and the count lowered until no chunk is empty.
+struct SplitPlan {
+  int64_t bh = 0;
+  int splits = 0;
+  int tiles_per_split = 0;
+  bool empty = true;
+};
+
+fa_status splitkv_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                       int64_t d, int64_t requested, SplitPlan* p) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (requested < 0) return FA_ERR_ARG;
+  p->empty = (B == 0 || H == 0 || Nq == 0);
+  if (p->empty) return FA_OK;
+  if (Nq > Nk || Nk > kMaxN) return FA_ERR_SHAPE;
+  if (B > std::numeric_limits<int64_t>::max() / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > ((int64_t)1 << 62) / (Nk * d)) return FA_ERR_SHAPE;
+  const int64_t tile = fa::kSplitKvTile;
+  const int64_t n_kt = (Nk + tile - 1) / tile;
+  const int64_t base = bh * ((Nq + 31) / 32);
+  int64_t sp;
+  if (requested > 0) {
+    sp = std::min(requested, n_kt);
+  } else {
+    sp = std::max<int64_t>(1, (2048 + base - 1) / base);
+    sp = std::min(sp, std::max<int64_t>(1, n_kt / 8));
+  }
+  const int64_t tps = (n_kt + sp - 1) / sp;
+  sp = (n_kt + tps - 1) / tps;
+  if (base > (int64_t)0x7fffffff / sp) return FA_ERR_SHAPE;
+  // The chunk outputs must be addressable in int64 as well.
+  if (sp * bh > ((int64_t)1 << 62) / (Nq * (d + 1))) return FA_ERR_SHAPE;
+  p->bh = bh;
+  p->splits = (int)sp;
+  p->tiles_per_split = (int)tps;
+  return FA_OK;
+}
+
+// Workspace of the split-KV forward: the chunk outputs (float, d per row)
+// then the chunk logsumexps.
+size_t splitkv_ws_bytes(const SplitPlan& p, int64_t Nq, int64_t d) {
+  const size_t rows = (size_t)p.splits * (size_t)p.bh * (size_t)Nq;
+  return rows * (size_t)d * 4 + (rows * 4 + 15) / 16 * 16;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t fa_fwd_splitkv_chunks(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t d, int64_t n_splits) {
+  SplitPlan p;
+  if (splitkv_plan(B, H, Nq, Nk, d, n_splits, &p) != FA_OK || p.empty) return 0;
+  return p.splits;
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq,
+                                      int64_t Nk, int64_t d, int64_t n_splits) {
+  SplitPlan p;
+  if (splitkv_plan(B, H, Nq, Nk, d, n_splits, &p) != FA_OK || p.empty) return 0;
+  return splitkv_ws_bytes(p, Nq, d);
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                         int64_t d, fa_dtype dt, float scale, int causal,
+                         int64_t n_splits, void* stream) {
+  if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_DTYPE;
+  SplitPlan p;
+  fa_status st = splitkv_plan(B, H, Nq, Nk, d, n_splits, &p);
+  if (st != FA_OK) return st;
+  if (!scale_ok(scale)) return FA_ERR_ARG;
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (p.empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(lse, 4) || !aligned(workspace, 16)) {
+    return FA_ERR_ALIGN;
+  }
+  if (workspace_bytes < splitkv_ws_bytes(p, Nq, d)) return FA_ERR_ARG;
+  fa::SplitKvArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + (size_t)p.splits * (size_t)p.bh * (size_t)Nq * (size_t)d;
+  a.bh = p.bh;
+  a.nq = (int)Nq;
+  a.nk = (int)Nk;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.n_splits = p.splits;
+  a.tiles_per_split = p.tiles_per_split;
+  return from_hip(fa::launch_splitkv_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o,
                  float* lse, int64_t B, int64_t H, int64_t N, int64_t d,

@@ -54,12 +54,12 @@
 namespace fa {
 namespace {
 
-template <int D_, int NW_>
+template <int D_, int NW_, int BC_ = (D_ == 128) ? 64 : 128>
 struct FwdTile {
   static constexpr int D = D_;
   static constexpr int NW = NW_;                      // waves per workgroup
   static constexpr int BR = 32 * NW;                  // query rows per workgroup
-  static constexpr int BC = (D == 128) ? 64 : 128;    // keys per tile
+  static constexpr int BC = BC_;                      // keys per tile
   static constexpr int KS = D / 16;                   // MFMA k-steps over d
   static constexpr int KB = BC / 32;                  // 32-key blocks per tile
   static constexpr int KK = BC / 16;                  // 16-key k-steps of PV
@@ -161,13 +161,15 @@ struct FwdWave {
   float m, m_use, l;
   int koff[T::KS];     // K fragment LDS offsets
   int voff[T::DB];     // V^T fragment (transpose read) LDS offsets
-  int qw0, qrow, h, n;
+  // n: query rows; nk: keys; q_off: the position of query row 0 in the key
+  // sequence (the causal rule is key <= q_off + row).
+  int qw0, qrow, h, n, nk, q_off;
   float c_log2;
 
   __device__ __forceinline__ FwdWave(const bf16* Qh, int qw0_, int lane, int n_,
-                                     float c_log2_)
+                                     int nk_, int q_off_, float c_log2_)
       : m(-INFINITY), m_use(0.f), l(0.f), qw0(qw0_), qrow(qw0_ + (lane & 31)),
-        h(lane >> 5), n(n_), c_log2(c_log2_) {
+        h(lane >> 5), n(n_), nk(nk_), q_off(q_off_), c_log2(c_log2_) {
     const int l32 = lane & 31;
     // Slot j of k-step ks is Q[qrow][ks*16 + h*8 + j].
 #pragma unroll
@@ -214,14 +216,14 @@ struct FwdWave {
   // Whether the tile starting at key kbase has keys past the diagonal or
   // past the sequence end for some row of this wave (wave-uniform).
   __device__ __forceinline__ bool needs_mask(int kbase) const {
-    return (CAUSAL && kbase + T::BC - 1 > qw0) || (kbase + T::BC > n);
+    return (CAUSAL && kbase + T::BC - 1 > q_off + qw0) || (kbase + T::BC > nk);
   }
   // Set those keys to -inf.  lim is the last visible key of the lane's row
   // relative to the key in register 0 of block 0; register i of block kb
   // holds key kb*32 + (i/4)*8 + (i%4) relative to it.
   __device__ __forceinline__ void apply_mask(f32x16 (&s)[T::KB],
                                              int kbase) const {
-    const int lim = (CAUSAL ? min(qrow, n - 1) : n - 1) - kbase - h * 4;
+    const int lim = (CAUSAL ? min(q_off + qrow, nk - 1) : nk - 1) - kbase - h * 4;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
 #pragma unroll
@@ -310,73 +312,49 @@ struct FwdWave {
       lse_h[qrow] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }
+  // The same result over one chunk of the keys, kept in fp32 for the merge:
+  // O_s = acc / l (0 if the chunk shows the row no key) and its logsumexp.
+  __device__ __forceinline__ void store_partial(float* Os, float* lse_s) const {
+    const float l_tot = sum_halves(l);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow >= n) return;
+    float* orow = Os + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                         acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + g * 8 + h * 4) = v;
+      }
+    }
+    if (h == 0) {
+      lse_s[qrow] = (l_tot > 0.f) ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
 };
 
-// Workgroup coordinates (head, first query row).
-struct FwdPlace {
-  int head, q0;
-};
-template <bool CAUSAL>
-__device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br) {
-  const int lid = xcd_logical_id(blockIdx.x, total);
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
-  return {lid / n_qtiles, qt * br};
-}
-
-// Every wave runs the same pipeline step per key tile:
+// The key loop of one workgroup: key tiles first, next_on(first), ... up to
+// kt_end (exclusive), K and V of the keys filled into kbuf / vbuf (two
+// buffers each), each wave's online-softmax state in wv.  Every wave runs
+// the same pipeline step per key tile:
 //   block A: the scores of tile `nxt` on the matrix cores while the vector
 //            units form tile `cur`'s probabilities;
 //   block B: tile `cur`'s PV product on the matrix cores while the vector
 //            units mask and reduce tile `nxt`'s scores.
-// With d = 128 (dense) a workgroup has 8 waves, one workgroup per CU: 256
-// query rows share each K/V tile, halving the tile traffic into LDS per row.
-// Otherwise a workgroup has 4 waves and two run per CU; the block-sparse
-// kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
-// row of the mask.
-template <int D, int NW, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                     const bf16* __restrict__ V, bf16* __restrict__ O,
-                     float* __restrict__ LSE, int n, int n_qtiles, int total,
-                     float c_log2, const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n) {
-  using T = FwdTile<D, NW>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
-  unsigned char* const kbuf = smem;                  // K0 | K1
-  unsigned char* const vbuf = smem + 2 * T::K_BYTES;  // V0 | V1
-
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR);
-  const int64_t hoff = (int64_t)pl.head * n * D;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const TileFill<T> fill(w, lane);
-  FwdWave<T, CAUSAL> wv(Q + hoff, pl.q0 + 32 * w, lane, n, c_log2);
-
-  // Key tiles to visit, in order.
-  const int n_ktiles = (n + T::BC - 1) / T::BC;
-  int kt_end = n_ktiles;
-  if (CAUSAL) kt_end = min(n_ktiles, (min(pl.q0 + T::BR, n) - 1) / T::BC + 1);
-  const uint8_t* mrow =
-      SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : nullptr;
-  // (readfirstlane keeps the index opaque to induction-variable rewriting,
-  // which would otherwise turn every DMA source into a loop-carried 64-bit
-  // pointer and exhaust the register file.)
-  auto next_on = [&](int kt) -> int {
-    ++kt;
-    if constexpr (SPARSE) {
-      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
-    }
-    return __builtin_amdgcn_readfirstlane(kt);
-  };
-
-  int cur = next_on(-1);
+template <class T, bool CAUSAL, class NextOn>
+__device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL>& wv,
+                                         const TileFill<T>& fill,
+                                         unsigned char* kbuf, unsigned char* vbuf,
+                                         const bf16* Kh, const bf16* Vh,
+                                         int n_keys, int first, int kt_end,
+                                         NextOn next_on) {
+  int cur = first;
   if (cur < kt_end) {
     int nxt = next_on(cur);
-    fill.k(Kh, cur * T::BC, n, kbuf);
-    fill.v(Vh, cur * T::BC, n, vbuf);
-    if (nxt < kt_end) fill.k(Kh, nxt * T::BC, n, kbuf + T::K_BYTES);
+    fill.k(Kh, cur * T::BC, n_keys, kbuf);
+    fill.v(Vh, cur * T::BC, n_keys, vbuf);
+    if (nxt < kt_end) fill.k(Kh, nxt * T::BC, n_keys, kbuf + T::K_BYTES);
     wait_dma();
     __syncthreads();
     // sa holds the current tile's scores; the next tile's scores go to sb
@@ -405,8 +383,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       int nxt2 = kt_end;
       if constexpr (NEXT) {
         nxt2 = next_on(nxt);
-        if (nxt2 < kt_end) fill.k(Kh, nxt2 * T::BC, n, kbuf + kb_cur * T::K_BYTES);
-        fill.v(Vh, nxt * T::BC, n, vbuf + (kb_cur ^ 1) * T::K_BYTES);
+        if (nxt2 < kt_end) fill.k(Kh, nxt2 * T::BC, n_keys, kbuf + kb_cur * T::K_BYTES);
+        fill.v(Vh, nxt * T::BC, n_keys, vbuf + (kb_cur ^ 1) * T::K_BYTES);
       }
       if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
       bf16x8 pf[T::KK];
@@ -450,6 +428,63 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     step(no{}, no{}, par_rt{}, it, sa, sb);
   }
+}
+
+// Workgroup coordinates (head, first query row).
+struct FwdPlace {
+  int head, q0;
+};
+template <bool CAUSAL>
+__device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br) {
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  return {lid / n_qtiles, qt * br};
+}
+
+// With d = 128 (dense) a workgroup has 8 waves, one workgroup per CU: 256
+// query rows share each K/V tile, halving the tile traffic into LDS per row.
+// Otherwise a workgroup has 4 waves and two run per CU; the block-sparse
+// kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
+// row of the mask.
+template <int D, int NW, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, bf16* __restrict__ O,
+                     float* __restrict__ LSE, int n, int n_qtiles, int total,
+                     float c_log2, const uint8_t* __restrict__ mask,
+                     int mask_cols, int block_m, int block_n) {
+  using T = FwdTile<D, NW>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
+  unsigned char* const kbuf = smem;                  // K0 | K1
+  unsigned char* const vbuf = smem + 2 * T::K_BYTES;  // V0 | V1
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR);
+  const int64_t hoff = (int64_t)pl.head * n * D;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const TileFill<T> fill(w, lane);
+  FwdWave<T, CAUSAL> wv(Q + hoff, pl.q0 + 32 * w, lane, n, n, 0, c_log2);
+
+  // Key tiles to visit, in order.
+  const int n_ktiles = (n + T::BC - 1) / T::BC;
+  int kt_end = n_ktiles;
+  if (CAUSAL) kt_end = min(n_ktiles, (min(pl.q0 + T::BR, n) - 1) / T::BC + 1);
+  const uint8_t* mrow =
+      SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : nullptr;
+  // (readfirstlane keeps the index opaque to induction-variable rewriting,
+  // which would otherwise turn every DMA source into a loop-carried 64-bit
+  // pointer and exhaust the register file.)
+  auto next_on = [&](int kt) -> int {
+    ++kt;
+    if constexpr (SPARSE) {
+      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
+    }
+    return __builtin_amdgcn_readfirstlane(kt);
+  };
+
+  key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on);
   wv.store(O + hoff, LSE + (int64_t)pl.head * n);
 }
 
@@ -476,10 +511,121 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
                   : launch_fwd<D, false, false>(a, s);
 }
 
+// Split-KV forward for a short block of queries against a long key
+// sequence: with few query rows the query tiles alone leave most of the
+// chip idle, so the keys are also cut into chunks handled by separate
+// workgroups ([REAPER] section 3.6, decoding).  Each workgroup is one wave:
+// 32 query rows against the key tiles of one chunk, 32 keys per tile so that
+// five of them fit a CU's LDS and keep enough K/V bytes in flight.  It writes
+// the chunk's normalised fp32 output and its logsumexp; splitkv_merge_kernel
+// combines the chunks.  The queries are the last nq of the nk positions, so
+// under the causal rule query i sees keys j <= nk - nq + i.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void splitkv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                         const bf16* __restrict__ V, float* __restrict__ Opart,
+                         float* __restrict__ LSEpart, int nq, int nk,
+                         int n_qtiles, int n_splits, int tiles_per_split,
+                         int total, int64_t bh, float c_log2) {
+  using T = FwdTile<D, 1, kSplitKvTile>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
+  unsigned char* const kbuf = smem;
+  unsigned char* const vbuf = smem + 2 * T::K_BYTES;
+
+  const int lane = threadIdx.x;
+  // Query tiles of one (head, chunk) are adjacent in the logical order and
+  // so run on one XCD, sharing the chunk's K/V in its L2.
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  const int qt = lid % n_qtiles;
+  const int split = (lid / n_qtiles) % n_splits;
+  const int head = lid / n_qtiles / n_splits;
+  const int q_off = nk - nq;
+  const bf16* Kh = K + (int64_t)head * nk * D;
+  const bf16* Vh = V + (int64_t)head * nk * D;
+  FwdWave<T, CAUSAL> wv(Q + (int64_t)head * nq * D, qt * 32, lane, nq, nk,
+                        q_off, c_log2);
+  const TileFill<T> fill(0, lane);
+
+  const int n_ktiles = (nk + T::BC - 1) / T::BC;
+  const int kt0 = split * tiles_per_split;
+  int kt_end = min(kt0 + tiles_per_split, n_ktiles);
+  if (CAUSAL) kt_end = min(kt_end, (q_off + min(qt * 32 + 32, nq) - 1) / T::BC + 1);
+  auto next_on = [](int kt) -> int { return __builtin_amdgcn_readfirstlane(kt + 1); };
+  key_loop(wv, fill, kbuf, vbuf, Kh, Vh, nk, kt0, kt_end, next_on);
+
+  const int64_t prow = ((int64_t)split * bh + head) * nq;
+  wv.store_partial(Opart + prow * D, LSEpart + prow);
+}
+
+// Merge of the chunk results of one query row by the two-part softmax rule
+// ([XYZ], incremental softmax tracking), applied to all chunks at once: with
+// M = max_s lse_s and w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
+// lse = M + ln sum_s w_s (each O_s is already divided by its own exp-sum, so
+// the weights are the chunks' exp-sums relative to M).  A row no chunk shows
+// any key gets O = 0 and lse = -inf.  D/4 lanes per row, four columns each.
+template <int D>
+__global__ __launch_bounds__(256)
+void splitkv_merge_kernel(const float* __restrict__ Opart,
+                          const float* __restrict__ LSEpart, bf16* __restrict__ O,
+                          float* __restrict__ LSE, int64_t rows, int n_splits) {
+  constexpr int LPR = D / 4;
+  constexpr int RPW = 256 / LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / LPR;
+  const int c = (threadIdx.x % LPR) * 4;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, LSEpart[s * rows + row]);
+  float sum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float w = fast_exp2((LSEpart[s * rows + row] - mx) * kLog2e);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(
+          Opart + (s * rows + row) * D + c);
+      sum += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, o[i], acc[i]);
+    }
+  }
+  const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
+  u32x2 vv;
+  vv[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+  vv[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(O + row * D + c) = vv;
+  if (c == 0) LSE[row] = (sum > 0.f) ? mx + fast_log2(sum) * kLn2 : -INFINITY;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_splitkv_t(const SplitKvArgs& a, hipStream_t s) {
+  const int n_qtiles = (a.nq + 31) / 32;
+  const int total = (int)(a.bh * a.n_splits * n_qtiles);
+  hipError_t e = launch_kernel(
+      splitkv_bf16_kernel<D, CAUSAL>, dim3(total), dim3(64), s,
+      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.ws_o, a.ws_lse,
+      a.nq, a.nk, n_qtiles, a.n_splits, a.tiles_per_split, total, a.bh,
+      a.scale * kLog2e);
+  if (e != hipSuccess) return e;
+  const int64_t rows = a.bh * a.nq;
+  constexpr int RPW = 256 / (D / 4);
+  return launch_kernel(splitkv_merge_kernel<D>, dim3((unsigned)((rows + RPW - 1) / RPW)),
+                       dim3(256), s, (const float*)a.ws_o,
+                       (const float*)a.ws_lse, (bf16*)a.o, a.lse, rows,
+                       a.n_splits);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   return a.d == 128 ? dispatch_mask<128>(a, s) : dispatch_mask<64>(a, s);
+}
+
+hipError_t launch_splitkv_bf16(const SplitKvArgs& a, hipStream_t s) {
+  if (a.d == 128) {
+    return a.causal ? launch_splitkv_t<128, true>(a, s)
+                    : launch_splitkv_t<128, false>(a, s);
+  }
+  return a.causal ? launch_splitkv_t<64, true>(a, s)
+                  : launch_splitkv_t<64, false>(a, s);
 }
 
 }  // namespace fa

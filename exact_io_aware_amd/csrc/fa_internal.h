@@ -48,7 +48,30 @@ struct BwdArgs {
   int block_n;             // multiple of 128
 };
 
+// Split-KV forward: nq queries (the last nq of the nk positions) against nk
+// keys, the keys cut into n_splits chunks of tiles_per_split tiles of
+// kSplitKvTile keys, every chunk non-empty.
+constexpr int kSplitKvTile = 32;
+struct SplitKvArgs {
+  const void* q;           // bh x nq x d
+  const void* k;           // bh x nk x d
+  const void* v;           // bh x nk x d
+  void* o;                 // bh x nq x d
+  float* lse;              // bh x nq
+  float* ws_o;             // n_splits x bh x nq x d: chunk outputs
+  float* ws_lse;           // n_splits x bh x nq: chunk logsumexps
+  int64_t bh;
+  int nq;
+  int nk;
+  int d;
+  float scale;
+  int causal;
+  int n_splits;
+  int tiles_per_split;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_splitkv_bf16(const SplitKvArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);

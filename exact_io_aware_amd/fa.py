@@ -16,8 +16,9 @@ import torch
 from . import _build
 
 __all__ = [
-    "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse",
-    "fa_bwd_preprocess",
+    "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv",
+    "fa_fwd_splitkv_chunks", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
+    "fa_bwd_blocksparse", "fa_bwd_preprocess",
     "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
     "fa_version", "library", "LIB_PATH",
 ]
@@ -53,6 +54,8 @@ def library():
         "fa_fwd": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P],
         "fa_fwd_blocksparse": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
                                I64, I64, P],
+        "fa_fwd_splitkv": [P, P, P, P, P, P, SZ, I64, I64, I64, I64, I64, I,
+                           F, I, I64, P],
         "fa_bwd": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F,
                    I, P],
         "fa_bwd_blocksparse": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
@@ -68,6 +71,10 @@ def library():
         fn.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.fa_bwd_workspace_bytes.restype = SZ
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [I64] * 6
+    lib.fa_fwd_splitkv_workspace_bytes.restype = SZ
+    lib.fa_fwd_splitkv_chunks.argtypes = [I64] * 6
+    lib.fa_fwd_splitkv_chunks.restype = I64
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -172,6 +179,55 @@ def fa_fwd_blocksparse(q, k, v, block_mask, block_m=128, block_n=128,
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
             _dtype_code(q), _scale(scale, d), int(bool(causal)),
             _ptr(mask_t), int(block_m), int(block_n), _stream(q.device)))
+    return o, lse_t
+
+
+def fa_fwd_splitkv_chunks(B, H, Nq, Nk, d, n_splits=0):
+    """Number of key chunks fa_fwd_splitkv uses (0 for empty/invalid)."""
+    return int(library().fa_fwd_splitkv_chunks(B, H, Nq, Nk, d, n_splits))
+
+
+def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits=0):
+    return int(library().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d,
+                                                        n_splits))
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=0,
+                   workspace=None, out=None, lse=None):
+    """Split-KV forward: q is B x H x Nq x d, k and v B x H x Nk x d (bf16).
+
+    The queries are the last Nq positions of the key sequence (causal: query
+    i sees keys j <= Nk - Nq + i).  ``n_splits`` caps the number of key
+    chunks (0 = automatic).  Returns O (B x H x Nq x d) and LSE (B x H x Nq).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("tensors must be B x H x N x d")
+    B, H, Nq, d = q.shape
+    Bk, Hk, Nk, dk = k.shape
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k "
+                         f"{tuple(k.shape)} v {tuple(v.shape)}")
+    for t in (q, k, v):
+        if t.dtype != q.dtype:
+            raise ValueError("all of Q, K, V must share one dtype")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("tensors must be on the same GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (d fastest)")
+    lib = library()
+    need = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    o = torch.empty_like(q) if out is None else out
+    lse_t = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+             if lse is None else lse)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_splitkv(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(workspace),
+            ws_bytes, B, H, Nq, Nk, d, _dtype_code(q), _scale(scale, d),
+            int(bool(causal)), int(n_splits), _stream(q.device)))
     return o, lse_t
 
 

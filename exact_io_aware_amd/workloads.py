@@ -15,6 +15,10 @@ Recipe (the same for every workload):
     off-diagonal blocks, round(frac * (T*T - T)), drawn without replacement by
     ``numpy.random.default_rng(seed)``.
 
+Decoding workloads (one or a few new query tokens against a long context)
+draw Q of shape (B, H, Nq, d) first, then K and V of shape (B, H, Nk, d),
+from the same kind of generator.
+
 Shapes follow the pages' workloads: a small fp32 single head (the simplified
 one-row-per-block kernel of the page "FlashAttention：在线 softmax 与
 IO-aware 注意力" runs fp32 at d = 64), the GPT-2 head shape at sequence 1K
@@ -29,8 +33,8 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["WORKLOADS", "workload", "make_inputs", "block_mask",
-           "workload_mask"]
+__all__ = ["WORKLOADS", "DECODE_WORKLOADS", "workload", "make_inputs",
+           "make_decode_inputs", "block_mask", "workload_mask"]
 
 
 def _w(name, B, H, N, d, dtype, causal, passes, seed, sigma=1.0,
@@ -57,7 +61,21 @@ WORKLOADS = {
 }
 
 
+# Decoding: one new token per sequence against a 16K-token context, 16
+# sequences of 32 heads of d = 128 (the long-context d = 128 head shape of
+# the workloads above; [REAPER] section 3.6 describes the decoding shape, a
+# single query row against the full K and V, without sizes).
+DECODE_WORKLOADS = {
+    "decode_16x32x1x16384x128": dict(
+        name="decode_16x32x1x16384x128", B=16, H=32, Nq=1, Nk=16384, d=128,
+        dtype="bf16", causal=(True,), passes=("decode",), seed=6, sigma=1.0,
+        scale=1.0 / math.sqrt(128)),
+}
+
+
 def workload(name):
+    if name in DECODE_WORKLOADS:
+        return dict(DECODE_WORKLOADS[name])
     return dict(WORKLOADS[name])
 
 
@@ -75,6 +93,20 @@ def make_inputs(B, H, N, d, seed, sigma=1.0, dtype="bf16", with_do=False,
     out = {}
     for n in names:
         x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x = x * sigma
+        out[n] = x.to(_DTYPES[dtype]).to(device)
+    return out
+
+
+def make_decode_inputs(B, H, Nq, Nk, d, seed, sigma=1.0, dtype="bf16",
+                       device="cpu"):
+    """Q (B, H, Nq, d), then K and V (B, H, Nk, d), drawn as described in the
+    module docstring."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = {}
+    for n, rows in (("q", Nq), ("k", Nk), ("v", Nk)):
+        x = torch.randn((B, H, rows, d), generator=g, dtype=torch.float32)
         if sigma != 1.0:
             x = x * sigma
         out[n] = x.to(_DTYPES[dtype]).to(device)

@@ -22,7 +22,7 @@
  *   B x H x N x d (d fastest, no padding): element (b, h, i, c) sits at
  *   offset ((b*H + h)*N + i)*d + c.  LSE and the backward workspace rows are
  *   B x H x N float32 arrays in the same (b, h, i) order.  Queries and keys
- *   have the same length N.
+ *   have the same length N (except in fa_fwd_splitkv).
  * Pointers.  Every tensor pointer is a device pointer owned by the caller,
  *   aligned to 16 bytes.  The library allocates no device memory and keeps no
  *   mutable global state; concurrent calls on different streams are safe as
@@ -106,6 +106,49 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
                              int64_t N, int64_t d, fa_dtype dt, float scale,
                              int causal, const uint8_t* mask, int64_t block_m,
                              int64_t block_n, void* stream);
+
+/*
+ * fa_fwd_splitkv — forward pass of a short block of queries against a long
+ * key sequence (decoding: one or a few new tokens against the whole
+ * context), with the keys cut into chunks processed in parallel ([REAPER]
+ * section 3.6) and the chunk results combined by the two-part softmax rule
+ * m = max(m1, m2), l = e^(m1 - m) l1 + e^(m2 - m) l2 ([XYZ], incremental
+ * softmax tracking).  Result as fa_fwd on the same rows:
+ *   O_i = sum_j softmax(S_i)_j v_j,  lse_i = ln sum_j exp(S_ij),
+ * S_ij = scale * q_i . k_j, up to rounding order.
+ *
+ * q          : input, B x H x Nq x d bfloat16.
+ * k, v       : inputs, B x H x Nk x d bfloat16, 1 <= Nq <= Nk (when B, H
+ *              and Nq are nonzero; Nq > Nk is FA_ERR_SHAPE).
+ * o          : output, B x H x Nq x d bfloat16.
+ * lse        : output, B x H x Nq float32.
+ * causal     : the queries are the last Nq positions of the sequence: query
+ *              i sees key j iff j <= Nk - Nq + i.  With Nq = Nk this is the
+ *              causal rule of fa_fwd.
+ * n_splits   : >= 0.  0 picks the chunk count from the shape; a positive
+ *              value caps it.  The count actually used is
+ *              fa_fwd_splitkv_chunks(); every chunk holds at least one
+ *              32-key tile.
+ * workspace  : caller-owned device scratch of at least
+ *              fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits)
+ *              bytes, 16-byte aligned; contents on entry ignored.  Holds the
+ *              chunk outputs (float32) and chunk logsumexps.
+ * Two kernels run in order on `stream`: the chunk pass and the merge.
+ * FA_BF16 only (FA_F32 returns FA_ERR_UNSUPPORTED); FA_ERR_ARG for negative
+ * n_splits, a bad scale or a short workspace.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                         int64_t d, fa_dtype dt, float scale, int causal,
+                         int64_t n_splits, void* stream);
+
+/* Key chunks fa_fwd_splitkv uses for this shape and n_splits, and the bytes
+ * of workspace it needs (both 0 for empty or invalid shapes). */
+int64_t fa_fwd_splitkv_chunks(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t d, int64_t n_splits);
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq,
+                                      int64_t Nk, int64_t d, int64_t n_splits);
 
 /*
  * fa_bwd — backward pass by recomputation ([TLDR] backward section; [XYZ]

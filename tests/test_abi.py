@@ -186,3 +186,63 @@ def test_bwd_blocksparse_validation(lib):
         assert bwd_sparse(lib, **{name: None}) == FA_ERR_NULL, name
     assert bwd_sparse(lib, dk=MISALIGNED) == FA_ERR_ALIGN
     assert bwd_sparse(lib, N=0, q=None, ws=None) == FA_OK
+
+
+def splitkv(lib, q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=None, B=2, H=3,
+            Nq=1, Nk=1000, d=128, dt=BF16, scale=0.09, causal=0, splits=0):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, splits)
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d,
+                              dt, scale, causal, splits, None)
+
+
+def test_splitkv_validation(lib):
+    assert splitkv(lib, B=-1) == FA_ERR_SHAPE
+    assert splitkv(lib, Nk=-1) == FA_ERR_SHAPE
+    assert splitkv(lib, Nq=5, Nk=4) == FA_ERR_SHAPE        # more queries than keys
+    assert splitkv(lib, Nk=(1 << 30) + 1) == FA_ERR_SHAPE
+    assert splitkv(lib, B=1 << 40, H=1 << 20) == FA_ERR_SHAPE
+    assert splitkv(lib, dt=9) == FA_ERR_DTYPE
+    assert splitkv(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    assert splitkv(lib, d=96) == FA_ERR_UNSUPPORTED
+    assert splitkv(lib, splits=-1) == FA_ERR_ARG
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert splitkv(lib, scale=bad) == FA_ERR_ARG
+    for name in ("q", "k", "v", "o", "lse", "ws"):
+        assert splitkv(lib, **{name: None}) == FA_ERR_NULL, name
+    for name in ("q", "k", "v", "o", "ws"):
+        assert splitkv(lib, **{name: MISALIGNED}) == FA_ERR_ALIGN, name
+    assert splitkv(lib, lse=P + 2) == FA_ERR_ALIGN
+    need = lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1, 1000, 128, 0)
+    assert splitkv(lib, ws_bytes=need - 1) == FA_ERR_ARG
+    # empty problems: no pointer is looked at
+    for B, H, Nq in ((0, 3, 1), (2, 0, 1), (2, 3, 0)):
+        assert splitkv(lib, q=None, k=None, v=None, o=None, lse=None, ws=None,
+                       ws_bytes=0, B=B, H=H, Nq=Nq) == FA_OK
+
+
+def test_splitkv_chunk_plan(lib):
+    chunks = lib.fa_fwd_splitkv_chunks
+    wsb = lib.fa_fwd_splitkv_workspace_bytes
+    # 1000 keys = 32 tiles of 32 keys; a cap is honoured, and the tiles are
+    # spread evenly with no empty chunk: 32 tiles over at most 5 chunks is
+    # 7 tiles per chunk, hence 5 chunks; over at most 6 it is 6 tiles per
+    # chunk, hence 6; a cap above the tile count gives one tile per chunk.
+    assert chunks(1, 1, 1, 1000, 128, 5) == 5
+    assert chunks(1, 1, 1, 1000, 128, 6) == 6
+    assert chunks(1, 1, 1, 1000, 128, 7) == 7     # 5 tiles each, 7 chunks
+    assert chunks(1, 1, 1, 1000, 128, 1000) == 32
+    assert chunks(1, 1, 1, 1000, 128, 1) == 1
+    # Automatic: at least 8 tiles per chunk, and no more chunks than needed
+    # for about 2048 workgroups.
+    assert chunks(1, 1, 1, 1000, 128, 0) == 4
+    assert chunks(8, 32, 1, 16384, 128, 0) == 8
+    assert chunks(64, 64, 1, 16384, 128, 0) == 1
+    assert chunks(1, 1, 1, 16, 64, 0) == 1
+    # workspace: chunks * rows * (d floats) + the logsumexps, 16-B rounded
+    s = chunks(2, 3, 5, 1000, 64, 3)
+    rows = s * 2 * 3 * 5
+    assert wsb(2, 3, 5, 1000, 64, 3) == rows * 64 * 4 + (rows * 4 + 15) // 16 * 16
+    assert wsb(0, 3, 5, 1000, 64, 3) == 0
+    assert wsb(2, 3, 5, 4, 64, 3) == 0              # invalid: Nq > Nk
+    assert chunks(2, 3, 5, 4, 64, 3) == 0
