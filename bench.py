@@ -14,7 +14,9 @@ inputs already resident in device memory.  Prints one JSON line.
              (whole heads, forward + backward), as a reference only
 
 Options: --gpus N (only 1 is supported), --steps K, --warmup W,
---no-cpu-baseline, --workload NAME (any backward-capable workload),
+--no-cpu-baseline, --workload NAME (any backward-capable workload; a
+decoding workload such as decode_16x32x1x16384x128 instead times the split-KV
+forward and reports GB/s against the HBM peak),
 --calib-copy-mb M (launch one plain device copy of M MiB before timing, for
 hardware-counter calibration), --all (also time every other workload and
 print one extra JSON line per workload; not part of the driver contract).
@@ -81,6 +83,17 @@ def stored_traffic(kernel, workload):
     return float(m_b.group(1))
 
 
+def calib_copy(mb):
+    """One plain device copy of `mb` MiB (read and written once), the
+    reference for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(mb * (1 << 20) // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def time_workload(name, steps, warmup, calib_mb=0):
     import torch
 
@@ -101,11 +114,7 @@ def time_workload(name, steps, warmup, calib_mb=0):
     stream = torch.cuda.current_stream(dev)
 
     if calib_mb:
-        src = torch.ones(calib_mb * (1 << 20) // 4, **f32)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(calib_mb)
 
     names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
     ev = {n: [] for n in names}
@@ -222,7 +231,15 @@ def time_passes(name, steps, warmup):
     return out
 
 
-def time_decode(name, steps, warmup):
+def decode_bytes(w, Nq=None):
+    """Algorithmic HBM bytes of one decoding call: Q, K, V read once, O and
+    LSE written once (bf16 tensors, fp32 LSE)."""
+    Nq = w["Nq"] if Nq is None else Nq
+    return w["B"] * w["H"] * (2 * 2 * Nq * w["d"] + 2 * 2 * w["Nk"] * w["d"]
+                              + 4 * Nq)
+
+
+def time_decode(name, steps, warmup, keep=None):
     """Timing of the split-KV forward on a decoding workload (used by --all):
     the whole fa_fwd_splitkv call (chunk pass + merge), median over steps.
     The work is a matrix-vector product per head, bound by HBM bandwidth, so
@@ -237,6 +254,8 @@ def time_decode(name, steps, warmup):
     dev = torch.device("cuda:0")
     x = workloads.make_decode_inputs(B, H, Nq, Nk, d, w["seed"], w["sigma"],
                                      device=dev)
+    if keep is not None:
+        keep.update(x)
     ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0),
                      dtype=torch.uint8, device=dev)
     o = torch.empty_like(x["q"])
@@ -259,7 +278,7 @@ def time_decode(name, steps, warmup):
             times.append((a, b))
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
-        nbytes = B * H * (2 * Nq * d + 2 * 2 * Nk * d + 4 * Nq)
+        nbytes = decode_bytes(w)
         gbs = nbytes / (ms * 1e-3) / 1e9
         out.append(dict(workload=name, causal=causal, pass_="decode",
                         ms_median=ms, gbytes_per_s=gbs,
@@ -275,12 +294,7 @@ def cpu_baseline(name, budget_s=12.0, max_heads=8):
     import oracle
     from exact_io_aware_amd import workloads
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     w = workloads.workload(name)
     x = workloads.workload_inputs(name, with_do=True)
     causal = w["causal"][-1]
@@ -304,6 +318,84 @@ def cpu_baseline(name, budget_s=12.0, max_heads=8):
             "sample": (f"{heads} whole heads (b,h) of {name}, forward + "
                        f"backward, fp64 NumPy materialising S and P "
                        f"(full N^2 even where causal), {t_total:.1f} s")}
+
+
+def cpu_baseline_decode(name, x, budget_s=12.0, max_heads=512):
+    """The fp64 oracle's decoding attention on whole heads, on host cores
+    (inputs `x` as drawn for the GPU timing; each head is copied to the host
+    before its clock starts)."""
+    import oracle
+    from exact_io_aware_amd import workloads
+
+    threads = _blas_threads()
+    w = workloads.workload(name)
+    heads, t_total = 0, 0.0
+    for b in range(w["B"]):
+        for hh in range(w["H"]):
+            q, k, v = (x[n][b, hh].cpu().double().numpy()
+                       for n in ("q", "k", "v"))
+            t0 = time.perf_counter()
+            oracle.attention_decode_head(q, k, v, w["scale"], True)
+            t_total += time.perf_counter() - t0
+            heads += 1
+            if t_total >= budget_s or heads >= max_heads:
+                break
+        if t_total >= budget_s or heads >= max_heads:
+            break
+    per_head = decode_bytes(w) / (w["B"] * w["H"])
+    return {"value": per_head * heads / t_total / 1e9, "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"{heads} whole heads (b,h) of {name}, fp64 NumPy "
+                       f"decoding attention, {t_total:.2f} s")}
+
+
+def decode_line(args):
+    """The JSON line of a decoding workload (--workload decode_...)."""
+    from exact_io_aware_amd import workloads
+    w = workloads.workload(args.workload)
+    x = {}
+    r = time_decode(args.workload, args.steps, args.warmup, keep=x)[-1]
+    line = {
+        "metric": "split-KV decoding attention GB/s (bf16, HBM-bound)",
+        "value": round(r["gbytes_per_s"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_median"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w["B"], "H": w["H"],
+                   "Nq": w["Nq"], "Nk": w["Nk"], "d": w["d"],
+                   "causal": True, "chunks": r["chunks"],
+                   "seed": w["seed"], "sigma": w["sigma"]},
+        "roofline": {
+            "kernel": "splitkv_bf16_kernel + splitkv_merge_kernel",
+            "bound": "hbm",
+            "achieved": round(r["gbytes_per_s"], 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(r["frac_hbm_peak"], 4),
+            "traffic": stored_traffic("splitkv_bf16_kernel", args.workload),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline_decode(args.workload, x)
+    print(json.dumps(line), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return len(os.sched_getaffinity(0))
 
 
 def main():
@@ -334,6 +426,12 @@ def main():
     from exact_io_aware_amd import fa
     fa.library()
 
+    from exact_io_aware_amd import workloads as _wl
+    if args.workload in _wl.DECODE_WORKLOADS:
+        if args.calib_copy_mb:
+            calib_copy(args.calib_copy_mb)
+        decode_line(args)
+        return
     r = time_workload(args.workload, args.steps, args.warmup,
                       args.calib_copy_mb)
     B, H, N, d = r["B"], r["H"], r["N"], r["d"]
