@@ -120,7 +120,6 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
       return FA_ERR_MASK;
     }
   }
-  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (*empty) return FA_OK;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (int i = 0; i < 9; ++i) {
@@ -206,6 +205,18 @@ fa_status splitkv_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
 size_t splitkv_ws_bytes(const SplitPlan& p, int64_t Nq, int64_t d) {
   const size_t rows = (size_t)p.splits * (size_t)p.bh * (size_t)Nq;
   return rows * (size_t)d * 4 + (rows * 4 + 15) / 16 * 16;
+}
+
+// The three backward passes for the input dtype.
+hipError_t run_pre(const fa::BwdArgs& a, fa_dtype dt, hipStream_t s) {
+  return dt == FA_F32 ? fa::launch_bwd_preprocess_f32(a, s)
+                      : fa::launch_bwd_preprocess(a, s);
+}
+hipError_t run_dkdv(const fa::BwdArgs& a, fa_dtype dt, hipStream_t s) {
+  return dt == FA_F32 ? fa::launch_bwd_dkdv_f32(a, s) : fa::launch_bwd_dkdv(a, s);
+}
+hipError_t run_dq(const fa::BwdArgs& a, fa_dtype dt, hipStream_t s) {
+  return dt == FA_F32 ? fa::launch_bwd_dq_f32(a, s) : fa::launch_bwd_dq(a, s);
 }
 
 }  // namespace
@@ -297,7 +308,7 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                             workspace, workspace_bytes, B, H, N, d, dt, 1.f,
                             false, 0, &a, &empty);
   if (st != FA_OK || empty) return st;
-  return from_hip(fa::launch_bwd_preprocess(a, reinterpret_cast<hipStream_t>(stream)));
+  return from_hip(run_pre(a, dt, reinterpret_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v,
@@ -312,7 +323,7 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v,
                             workspace, workspace_bytes, B, H, N, d, dt, scale,
                             true, causal, &a, &empty);
   if (st != FA_OK || empty) return st;
-  return from_hip(fa::launch_bwd_dkdv(a, reinterpret_cast<hipStream_t>(stream)));
+  return from_hip(run_dkdv(a, dt, reinterpret_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
@@ -327,7 +338,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                             workspace, workspace_bytes, B, H, N, d, dt, scale,
                             true, causal, &a, &empty);
   if (st != FA_OK || empty) return st;
-  return from_hip(fa::launch_bwd_dq(a, reinterpret_cast<hipStream_t>(stream)));
+  return from_hip(run_dq(a, dt, reinterpret_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -342,11 +353,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                             true, causal, &a, &empty);
   if (st != FA_OK || empty) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = from_hip(fa::launch_bwd_preprocess(a, s));
+  st = from_hip(run_pre(a, dt, s));
   if (st != FA_OK) return st;
-  st = from_hip(fa::launch_bwd_dkdv(a, s));
+  st = from_hip(run_dkdv(a, dt, s));
   if (st != FA_OK) return st;
-  return from_hip(fa::launch_bwd_dq(a, s));
+  return from_hip(run_dq(a, dt, s));
 }
 
 fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
@@ -364,11 +375,11 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                             true);
   if (st != FA_OK || empty) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = from_hip(fa::launch_bwd_preprocess(a, s));
+  st = from_hip(run_pre(a, dt, s));
   if (st != FA_OK) return st;
-  st = from_hip(fa::launch_bwd_dkdv(a, s));
+  st = from_hip(run_dkdv(a, dt, s));
   if (st != FA_OK) return st;
-  return from_hip(fa::launch_bwd_dq(a, s));
+  return from_hip(run_dq(a, dt, s));
 }
 
 const char* fa_status_str(fa_status s) {
@@ -378,7 +389,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or overflowing size";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
     case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; backward needs bf16";
+      return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, or dtype not provided by this call";
     case FA_ERR_MASK:
       return "FA_ERR_MASK: block sizes must be positive multiples of 128";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";

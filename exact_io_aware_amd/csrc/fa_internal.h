@@ -76,5 +76,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+// float32 inputs (q, k, v, o, dout are float*).
+hipError_t launch_bwd_preprocess_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

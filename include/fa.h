@@ -34,7 +34,8 @@
  *   returns FA_OK (pointers are not inspected).  d must be 64 or 128.
  * dtype.  FA_BF16: Q, K, V, O, dO are bfloat16 (round-to-nearest-even
  *   storage), arithmetic is bf16 x bf16 products accumulated in float32.
- *   FA_F32: Q, K, V, O are float32 throughout (forward only).
+ *   FA_F32: Q, K, V, O, dO are float32 throughout (fa_fwd_splitkv is bf16
+ *   only).
  *   LSE, dQ, dK, dV and the workspace are always float32.
  * scale.  Finite and > 0 (the usual value is 1/sqrt(d), [Q67] section 1).
  * Causal.  causal != 0 makes key j visible to query i iff j <= i.
@@ -170,7 +171,10 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq,
  * workspace        : caller-owned device scratch of at least
  *                    fa_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
  *                    aligned; its contents on entry are ignored.
- * FA_BF16 only; FA_F32 returns FA_ERR_UNSUPPORTED.
+ * FA_BF16: bf16 inputs on the matrix cores (bf16 products, fp32
+ * accumulation; P and dS rounded to bf16 before their products).  FA_F32:
+ * float32 inputs, every product and sum in fp32 on the vector units (for
+ * accuracy, not speed).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse, float* dq, float* dk,

@@ -119,8 +119,15 @@ def bwd(lib, ws_bytes=None, **kw):
 def test_bwd_validation(lib):
     need = lib.fa_bwd_workspace_bytes(2, 3, 256, 128)
     assert need >= 2 * 2 * 3 * 256 * 4
-    assert bwd(lib, dt=F32) == FA_ERR_UNSUPPORTED
     assert bwd(lib, dt=9) == FA_ERR_DTYPE
+    # float32 runs the same checks (only failures are exercised here: a
+    # valid call would launch kernels)
+    assert bwd(lib, dt=F32, d=96) == FA_ERR_UNSUPPORTED
+    assert bwd(lib, dt=F32, ws_bytes=need - 4) == FA_ERR_ARG
+    assert bwd(lib, dt=F32, scale=0.0) == FA_ERR_ARG
+    for name in ("q", "dq", "ws"):
+        assert bwd(lib, dt=F32, **{name: None}) == FA_ERR_NULL, name
+        assert bwd(lib, dt=F32, **{name: MISALIGNED}) == FA_ERR_ALIGN, name
     assert bwd(lib, d=256) == FA_ERR_UNSUPPORTED
     assert bwd(lib, ws_bytes=need - 4) == FA_ERR_ARG
     assert bwd(lib, scale=float("nan")) == FA_ERR_ARG
@@ -179,7 +186,8 @@ def test_bwd_blocksparse_validation(lib):
     assert bwd_sparse(lib, bm=64) == FA_ERR_MASK
     assert bwd_sparse(lib, bn=200) == FA_ERR_MASK
     assert bwd_sparse(lib, bm=-128) == FA_ERR_MASK
-    assert bwd_sparse(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    assert bwd_sparse(lib, dt=F32, bm=64) == FA_ERR_MASK
+    assert bwd_sparse(lib, dt=F32, dv=None) == FA_ERR_NULL
     assert bwd_sparse(lib, scale=0.0) == FA_ERR_ARG
     assert bwd_sparse(lib, ws_bytes=16) == FA_ERR_ARG
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
