@@ -34,7 +34,8 @@ import numpy as np
 import torch
 
 __all__ = ["WORKLOADS", "DECODE_WORKLOADS", "workload", "make_inputs",
-           "make_decode_inputs", "block_mask", "workload_mask"]
+           "make_inputs_device", "make_decode_inputs", "block_mask",
+           "workload_mask"]
 
 
 def _w(name, B, H, N, d, dtype, causal, passes, seed, sigma=1.0,
@@ -96,6 +97,26 @@ def make_inputs(B, H, N, d, seed, sigma=1.0, dtype="bf16", with_do=False,
         if sigma != 1.0:
             x = x * sigma
         out[n] = x.to(_DTYPES[dtype]).to(device)
+    return out
+
+
+def make_inputs_device(B, H, N, d, seed, sigma=1.0, dtype="bf16",
+                       with_do=False, device="cuda:0"):
+    """Q, K, V (and dO) drawn on the device itself, for shapes too large to
+    draw on the host in reasonable time: a ``torch.Generator`` of that
+    device seeded with `seed` draws them in the order Q, K, V, dO with
+    ``torch.randn`` (float32), each multiplied by sigma and rounded to the
+    dtype.  (Not the same numbers as ``make_inputs`` for the same seed.)"""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    names = ("q", "k", "v", "do") if with_do else ("q", "k", "v")
+    out = {}
+    for n in names:
+        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32,
+                        device=device)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        out[n] = x.to(_DTYPES[dtype])
+        del x
     return out
 
 

@@ -7,6 +7,7 @@ leg may import this package.  It shares no code with the HIP library.
 from .attention import (  # noqa: F401
     attention_bwd,
     attention_bwd_head,
+    attention_bwd_rows,
     attention_decode_head,
     attention_fwd,
     attention_fwd_head,

@@ -46,6 +46,7 @@ __all__ = [
     "attention_fwd",
     "attention_bwd_head",
     "attention_bwd",
+    "attention_bwd_rows",
     "tiled_fwd_head",
     "tiled_fwd_fa1_head",
     "causal_tiles_visited",
@@ -217,6 +218,35 @@ def attention_bwd_head(q, k, v, do, scale, causal=False, block_mask=None,
         dq[r] = scale * (dS @ k)
         dk += scale * (dS.T @ q[r])
     return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, do, scale, rows, causal=False,
+                       block_mask=None, block_m=128, block_n=128):
+    """The backward restricted to a set of query rows, for heads too long to
+    materialise: dQ of those rows, and their contributions to dK and dV.
+
+    Same chain rule as ``attention_bwd_head``, applied to the rows given:
+    dQ_i depends only on row i of P and dP, so dQ[rows] is exact; dK and dV
+    are sums over query rows, so the returned dk_part = scale * dS[rows]^T
+    q[rows] and dv_part = P[rows]^T dO[rows] are the contributions of those
+    rows only (under the causal rule, the contributions of rows [N-T, N)
+    are the whole dK, dV of keys [N-T, N), which no earlier row sees).
+    Work and memory are O(len(rows) * N * d).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    r = np.asarray(rows, dtype=np.int64)
+    n_k = k.shape[0]
+    S = scale * (q[r] @ k.T)
+    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n), S,
+                 NEG_INF)
+    P, _, _ = _softmax_rows(S)
+    dP = do[r] @ v.T
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    dq_rows = scale * (dS @ k)
+    dk_part = scale * (dS.T @ q[r])
+    dv_part = P.T @ do[r]
+    return dq_rows, dk_part, dv_part
 
 
 def attention_bwd(Q, K, V, dO, scale, causal=False, block_mask=None,

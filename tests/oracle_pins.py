@@ -470,6 +470,45 @@ def check_decode(orc):
     _close(lse, Tl, 1e-12, "decode vs torch LSE")
 
 
+def check_bwd_rows(orc):
+    """The row-restricted backward against PyTorch's float64 autograd (mask
+    expanded here with Python loops): dQ of chosen rows equals the full dQ
+    at those rows; the rows' contributions to dK and dV, summed over a
+    partition of all rows, equal the full dK and dV; under the causal rule
+    the last T rows alone give the whole dK, dV of the last T keys.  Causal
+    and not, with and without a block mask."""
+    r = _rng(41)
+    n, d, dv, blk = 11, 5, 3, 4
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    v, do = r.standard_normal((n, dv)), r.standard_normal((n, dv))
+    bm = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    for causal in (False, True):
+        for mask in (None, bm):
+            elem = None
+            if mask is not None:
+                elem = np.array([[mask[i // blk][j // blk] != 0
+                                  for j in range(n)] for i in range(n)])
+            _, _, Tdq, Tdk, Tdv = _torch_reference(q, k, v, do, 0.7, causal,
+                                                   elem)
+            sel = [0, 3, 7, 10]
+            dq_rows, _, _ = orc.attention_bwd_rows(q, k, v, do, 0.7, sel,
+                                                   causal, mask, blk, blk)
+            _close(dq_rows, Tdq[sel], 1e-12, "bwd rows dQ")
+            dk_sum, dv_sum = np.zeros_like(k), np.zeros_like(v)
+            for part in ([0, 1, 2, 3, 4], [5, 6], [7, 8, 9, 10]):
+                _, dk_p, dv_p = orc.attention_bwd_rows(q, k, v, do, 0.7, part,
+                                                       causal, mask, blk, blk)
+                dk_sum += dk_p
+                dv_sum += dv_p
+            _close(dk_sum, Tdk, 1e-12, "bwd rows: dK contributions sum")
+            _close(dv_sum, Tdv, 1e-12, "bwd rows: dV contributions sum")
+            if causal:
+                _, dk_t, dv_t = orc.attention_bwd_rows(
+                    q, k, v, do, 0.7, [8, 9, 10], causal, mask, blk, blk)
+                _close(dk_t[8:], Tdk[8:], 1e-12, "causal tail keys dK")
+                _close(dv_t[8:], Tdv[8:], 1e-12, "causal tail keys dV")
+
+
 ALL_CHECKS = [
     check_fig1_divide_last,
     check_fig2_streamed_pairs,
@@ -487,4 +526,5 @@ ALL_CHECKS = [
     check_causal_tile_count,
     check_block_sparse,
     check_decode,
+    check_bwd_rows,
 ]

@@ -62,6 +62,16 @@ MUTATIONS = [
     ("tiled: causal block skip too eager",
      "return (not causal) or j0 <= i1 - 1", "return (not causal) or j0 <= i0",
      0),
+    ("bwd rows: scale dropped in S", "S = scale * (q[r] @ k.T)",
+     "S = (q[r] @ k.T)", 2),
+    ("bwd rows: D term dropped", "dS = P * (dP - D[:, None])", "dS = P * dP",
+     1),
+    ("bwd rows: dQ scale dropped", "dq_rows = scale * (dS @ k)",
+     "dq_rows = (dS @ k)", 0),
+    ("bwd rows: dK part without transpose", "dk_part = scale * (dS.T @ q[r])",
+     "dk_part = scale * (dS.T @ q)", 0),
+    ("bwd rows: dV part from P not transposed", "dv_part = P.T @ do[r]",
+     "dv_part = P.T @ do[r][::-1]", 0),
     ("FA1: old sum not rescaled", "l_new = c_old * l + c_blk * l_blk",
      "l_new = l + c_blk * l_blk", 0),
     ("FA1: output not un-normalised",
