@@ -120,6 +120,28 @@ def _shape4(*ts):
     return tuple(ref.shape)
 
 
+def _arg(t, name, shape, dtype, device):
+    """Check a caller-supplied tensor that the kernels read or write: exact
+    shape, dtype, device and contiguity (the library trusts its sizes)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got "
+                         f"{tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ws_arg(ws, device):
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the "
+                         "inputs' device")
+    return ws, ws.numel() * ws.element_size()
+
+
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -136,14 +158,38 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     """O, LSE = attention(q, k, v); q, k, v are B x H x N x d bf16 or fp32."""
     B, H, N, d = _shape4(q, k, v)
     lib = library()
-    o = torch.empty_like(q) if out is None else out
-    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-             if lse is None else lse)
+    o, lse_t = _fwd_outputs(q, (B, H, N, d), out, lse)
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B,
                           H, N, d, _dtype_code(q), _scale(scale, d),
                           int(bool(causal)), _stream(q.device)))
     return o, lse_t
+
+
+def _fwd_outputs(q, shape, out, lse):
+    """O (shape, q's dtype) and LSE (shape[:-1], float32): allocated, or the
+    caller's tensors after checking them."""
+    if out is None:
+        out = torch.empty(shape, dtype=q.dtype, device=q.device)
+    else:
+        _arg(out, "out", shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty(shape[:-1], dtype=torch.float32, device=q.device)
+    else:
+        _arg(lse, "lse", shape[:-1], torch.float32, q.device)
+    return out, lse
+
+
+def _grads(q, dq, dk, dv):
+    """dQ, dK, dV (float32, q's shape): allocated, or checked."""
+    res = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        else:
+            _arg(t, name, q.shape, torch.float32, q.device)
+        res.append(t)
+    return res
 
 
 def _mask_arg(block_mask, N, block_m, block_n, device):
@@ -171,9 +217,7 @@ def fa_fwd_blocksparse(q, k, v, block_mask, block_m=128, block_n=128,
     B, H, N, d = _shape4(q, k, v)
     lib = library()
     mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = (torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-             if lse is None else lse)
+    o, lse_t = _fwd_outputs(q, (B, H, N, d), out, lse)
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd_blocksparse(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
@@ -219,10 +263,8 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=0,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8,
                                 device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    o = torch.empty_like(q) if out is None else out
-    lse_t = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-             if lse is None else lse)
+    workspace, ws_bytes = _ws_arg(workspace, q.device)
+    o, lse_t = _fwd_outputs(q, (B, H, Nq, d), out, lse)
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd_splitkv(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(workspace),
@@ -239,7 +281,7 @@ def _workspace(B, H, N, d, device, workspace):
     need = fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    return _ws_arg(workspace, device)
 
 
 def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
@@ -247,10 +289,8 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
     """dQ, dK, dV (float32) of L = sum(O * dO), recomputing P from lse."""
     B, H, N, d = _shape4(q, k, v, o, do)
     lib = library()
-    f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.empty(q.shape, **f32) if dq is None else dq
-    dk = torch.empty(q.shape, **f32) if dk is None else dk
-    dv = torch.empty(q.shape, **f32) if dv is None else dv
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    dq, dk, dv = _grads(q, dq, dk, dv)
     ws, ws_bytes = _workspace(B, H, N, d, q.device, workspace)
     with torch.cuda.device(q.device):
         _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
@@ -268,10 +308,8 @@ def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, block_m=128,
     B, H, N, d = _shape4(q, k, v, o, do)
     lib = library()
     mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
-    f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.empty(q.shape, **f32) if dq is None else dq
-    dk = torch.empty(q.shape, **f32) if dk is None else dk
-    dv = torch.empty(q.shape, **f32) if dv is None else dv
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    dq, dk, dv = _grads(q, dq, dk, dv)
     ws, ws_bytes = _workspace(B, H, N, d, q.device, workspace)
     with torch.cuda.device(q.device):
         _check(lib.fa_bwd_blocksparse(
@@ -284,28 +322,32 @@ def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, block_m=128,
 
 def fa_bwd_preprocess(o, do, lse, workspace):
     B, H, N, d = _shape4(o, do)
+    _arg(lse, "lse", (B, H, N), torch.float32, o.device)
+    workspace, ws_bytes = _ws_arg(workspace, o.device)
     with torch.cuda.device(o.device):
         _check(library().fa_bwd_preprocess(
-            _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), B, H, N, d,
-            _dtype_code(o), _stream(o.device)))
+            _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace), ws_bytes, B, H, N,
+            d, _dtype_code(o), _stream(o.device)))
 
 
 def fa_bwd_dkdv(q, k, v, do, workspace, dk, dv, scale=None, causal=False):
     B, H, N, d = _shape4(q, k, v, do)
+    _arg(dk, "dk", q.shape, torch.float32, q.device)
+    _arg(dv, "dv", q.shape, torch.float32, q.device)
+    workspace, ws_bytes = _ws_arg(workspace, q.device)
     with torch.cuda.device(q.device):
         _check(library().fa_bwd_dkdv(
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), B,
-            H, N, d, _dtype_code(q), _scale(scale, d), int(bool(causal)),
-            _stream(q.device)))
+            _ptr(workspace), ws_bytes, B, H, N, d, _dtype_code(q),
+            _scale(scale, d), int(bool(causal)), _stream(q.device)))
 
 
 def fa_bwd_dq(q, k, v, do, workspace, dq, scale=None, causal=False):
     B, H, N, d = _shape4(q, k, v, do)
+    _arg(dq, "dq", q.shape, torch.float32, q.device)
+    workspace, ws_bytes = _ws_arg(workspace, q.device)
     with torch.cuda.device(q.device):
         _check(library().fa_bwd_dq(
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), B, H, N, d,
-            _dtype_code(q), _scale(scale, d), int(bool(causal)),
-            _stream(q.device)))
+            ws_bytes, B, H, N, d, _dtype_code(q), _scale(scale, d),
+            int(bool(causal)), _stream(q.device)))
