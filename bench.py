@@ -486,6 +486,9 @@ def main():
         for name in workloads.WORKLOADS:
             for res in time_passes(name, max(args.steps, 20), 3):
                 print(json.dumps(res), flush=True)
+        for name in workloads.CONTEXT_WORKLOADS:
+            for res in time_passes(name, max(args.steps, 20), 3):
+                print(json.dumps(res), flush=True)
         for name in workloads.DECODE_WORKLOADS:
             for res in time_decode(name, max(args.steps, 20), 3):
                 print(json.dumps(res), flush=True)

@@ -33,7 +33,8 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["WORKLOADS", "DECODE_WORKLOADS", "workload", "make_inputs",
+__all__ = ["WORKLOADS", "DECODE_WORKLOADS", "CONTEXT_WORKLOADS", "workload",
+           "make_inputs",
            "make_inputs_device", "make_decode_inputs", "block_mask",
            "workload_mask"]
 
@@ -74,9 +75,20 @@ DECODE_WORKLOADS = {
 }
 
 
+# Context: the single fp32 head (N = 2048, d = 64) on which the simplified
+# one-row-per-block kernel of the page "FlashAttention：在线 softmax 与
+# IO-aware 注意力" reports its time and its max-abs error against standard
+# attention (section 3).
+CONTEXT_WORKLOADS = {
+    "fp32_1x1x2048x64": _w("fp32_1x1x2048x64", 1, 1, 2048, 64, "f32",
+                           (False,), ("fwd",), seed=7),
+}
+
+
 def workload(name):
-    if name in DECODE_WORKLOADS:
-        return dict(DECODE_WORKLOADS[name])
+    for table in (DECODE_WORKLOADS, CONTEXT_WORKLOADS):
+        if name in table:
+            return dict(table[name])
     return dict(WORKLOADS[name])
 
 
@@ -164,7 +176,7 @@ def workload_mask(w):
 
 def workload_inputs(name, with_do=None, device="cpu"):
     """Inputs of a named workload (dO included for backward workloads)."""
-    w = WORKLOADS[name]
+    w = workload(name)
     if with_do is None:
         with_do = "bwd" in w["passes"]
     return make_inputs(w["B"], w["H"], w["N"], w["d"], w["seed"], w["sigma"],
