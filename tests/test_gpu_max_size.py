@@ -110,3 +110,27 @@ def test_max_size_fwd_noncausal_d64(dev):
         O, L = oracle.attention_fwd_head(qh, kh, vh, scale, False, rows=EDGE)
         _max_abs(f"O edge rows ({b},{h})", f64(o[b, h, EDGE]), O)
         _max_abs(f"LSE edge rows ({b},{h})", f64(lse[b, h, EDGE]), L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_tiny_heads(dev, d):
+    # 65536 heads of 16 rows: the largest grids (one workgroup per head in
+    # every pass) and per-head offsets up to 2^20 heads * 16 rows * d.
+    B, H, n = 256, 256, 16
+    scale = 1 / math.sqrt(d)
+    x = workloads.make_inputs_device(B, H, n, d, seed=10 + d, with_do=True,
+                                     device=dev)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
+        dq, dk, dv = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse,
+                               scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        for b, h in ((0, 0), (0, 255), (131, 77), (255, 255)):
+            args = [f64(x[k][b, h]) for k in ("q", "k", "v", "do")]
+            O, L = oracle.attention_fwd_head(*args[:3], scale, causal)
+            compare(f"O ({b},{h})", f64(o[b, h]), O)
+            compare(f"LSE ({b},{h})", f64(lse[b, h]), L)
+            for name, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv),
+                                    oracle.attention_bwd_head(*args, scale,
+                                                              causal)):
+                compare(f"{name} ({b},{h})", f64(got[b, h]), r)
