@@ -37,6 +37,8 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
   // at most 2^31 - 1 workgroups of >= 64 rows.
   if (bh_ > ((int64_t)1 << 62) / (N * d)) return FA_ERR_SHAPE;
   if (bh_ * ((N + 63) / 64) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+  // The row passes launch one workgroup per 8-16 rows.
+  if (bh_ * N > ((int64_t)1 << 34)) return FA_ERR_SHAPE;
   *bh = bh_;
   return FA_OK;
 }
@@ -192,6 +194,8 @@ fa_status splitkv_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
   const int64_t tps = (n_kt + sp - 1) / sp;
   sp = (n_kt + tps - 1) / tps;
   if (base > (int64_t)0x7fffffff / sp) return FA_ERR_SHAPE;
+  // The merge launches one workgroup per 8 (d = 128) or 16 rows.
+  if (bh * Nq > ((int64_t)1 << 34)) return FA_ERR_SHAPE;
   // The chunk outputs must be addressable in int64 as well.
   if (sp * bh > ((int64_t)1 << 62) / (Nq * (d + 1))) return FA_ERR_SHAPE;
   p->bh = bh;

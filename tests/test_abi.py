@@ -254,3 +254,13 @@ def test_splitkv_chunk_plan(lib):
     assert wsb(0, 3, 5, 1000, 64, 3) == 0
     assert wsb(2, 3, 5, 4, 64, 3) == 0              # invalid: Nq > Nk
     assert chunks(2, 3, 5, 4, 64, 3) == 0
+
+
+def test_row_count_limits(lib):
+    # 2^35 rows (2^30 heads of 32): every other size check passes, but the
+    # row passes and the split-KV merge would need more than 2^31
+    # workgroups; rejected up front.
+    assert fwd(lib, B=1 << 20, H=1 << 10, N=32) == FA_ERR_SHAPE
+    assert bwd(lib, B=1 << 20, H=1 << 10, N=32, d=64, ws_bytes=0) == FA_ERR_SHAPE
+    assert splitkv(lib, B=1 << 25, H=1 << 5, Nq=32, Nk=32, ws_bytes=0) == FA_ERR_SHAPE
+    assert lib.fa_fwd_splitkv_chunks(1 << 25, 1 << 5, 32, 32, 128, 0) == 0
