@@ -22,32 +22,45 @@
 namespace fa {
 namespace {
 
-template <int D>
+constexpr int kNumCus = 256;  // compute units of an MI355X
+
+// KSPLIT groups of lanes share the workgroup's rows and split every key
+// tile between them (group g takes keys 16g .. 16g + 15 of each 64-key
+// tile); their partial states are merged at the end by the two-part rule
+// ([XYZ], incremental softmax tracking).  KSPLIT = 4 is used when the
+// problem has too few rows to fill the chip, so that each lane walks a
+// quarter of the keys.
+template <int D, int KSPLIT = 1>
 struct F32Tile {
-  static constexpr int TPR = D / 32;       // lanes per query row
-  static constexpr int ROWS = 256 / TPR;   // query rows per workgroup
-  static constexpr int BC = 64;            // keys per LDS tile
-  static constexpr int CH = 16;            // keys per softmax update
+  static constexpr int TPR = D / 32;                // lanes per query row
+  static constexpr int GROUP = 256 / KSPLIT;        // lanes per key group
+  static constexpr int ROWS = GROUP / TPR;          // query rows per workgroup
+  static constexpr int BC = 64;                     // keys per LDS tile
+  static constexpr int CH = 16;                     // keys per softmax update
+  static_assert(KSPLIT == 1 || KSPLIT * CH == BC, "one chunk per group");
 };
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, int KSPLIT>
 __global__ __launch_bounds__(256)
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, float* __restrict__ O,
                     float* __restrict__ LSE, int n, int n_qtiles,
                     float c_log2, const uint8_t* __restrict__ mask,
                     int mask_cols, int block_m, int block_n) {
-  using T = F32Tile<D>;
-  __shared__ __attribute__((aligned(16))) float sK[T::BC * D];
-  __shared__ __attribute__((aligned(16))) float sV[T::BC * D];
+  using T = F32Tile<D, KSPLIT>;
+  __shared__ __attribute__((aligned(16))) float smem[2 * T::BC * D];
+  float* const sK = smem;
+  float* const sV = smem + T::BC * D;
 
   const int tid = threadIdx.x;
-  const int part = tid % T::TPR;
+  const int grp = tid / T::GROUP;       // key group (0 when KSPLIT = 1)
+  const int gtid = tid % T::GROUP;
+  const int part = gtid % T::TPR;
   const int head = blockIdx.x / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - blockIdx.x % n_qtiles)
                         : (blockIdx.x % n_qtiles);
   const int q0 = qt * T::ROWS;
-  const int qrow = q0 + tid / T::TPR;
+  const int qrow = q0 + gtid / T::TPR;
   const int64_t hoff = (int64_t)head * n * D;
   const int c0 = part * 32;  // first d coordinate owned by this lane
 
@@ -90,7 +103,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
     __syncthreads();
     const int kend = min(T::BC, n - kbase);
-    for (int k0 = 0; k0 < kend; k0 += T::CH) {
+    for (int k0 = grp * T::CH; k0 < kend; k0 += T::CH * KSPLIT) {
       float s[T::CH];
 #pragma unroll
       for (int j = 0; j < T::CH; ++j) {
@@ -140,6 +153,45 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     }
   }
 
+  if constexpr (KSPLIT > 1) {
+    // Groups 1.. leave (m, l, acc) in LDS; group 0 merges them: with
+    // M = max m_g, l = sum_g 2^(m_g - M) l_g and acc = sum_g 2^(m_g - M) acc_g.
+    __syncthreads();
+    float* st = smem;  // (KSPLIT - 1) x GROUP x (32 + 2) floats
+    constexpr int STR = 34;
+    static_assert((KSPLIT - 1) * T::GROUP * STR <= 2 * T::BC * D,
+                  "merge state fits in the tile space");
+    if (grp > 0) {
+      float* my = st + ((grp - 1) * T::GROUP + gtid) * STR;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) my[c] = acc[c];
+      my[32] = m;
+      my[33] = l;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    float mg[KSPLIT];
+    mg[0] = m;
+#pragma unroll
+    for (int g = 1; g < KSPLIT; ++g) mg[g] = st[((g - 1) * T::GROUP + gtid) * STR + 32];
+    float M = mg[0];
+#pragma unroll
+    for (int g = 1; g < KSPLIT; ++g) M = fmaxf(M, mg[g]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float a0 = fast_exp2(m - M_use);
+    l *= a0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) acc[c] *= a0;
+#pragma unroll
+    for (int g = 1; g < KSPLIT; ++g) {
+      const float* o = st + ((g - 1) * T::GROUP + gtid) * STR;
+      const float a = fast_exp2(mg[g] - M_use);
+      l = fmaf(a, o[33], l);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) acc[c] = fmaf(a, o[c], acc[c]);
+    }
+    m = M;
+  }
   if (qrow < n) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     float* orow = O + hoff + (int64_t)qrow * D + c0;
@@ -156,16 +208,27 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  using T = F32Tile<D>;
+template <int D, bool CAUSAL, bool SPARSE, int KSPLIT>
+hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+  using T = F32Tile<D, KSPLIT>;
   const int n_qtiles = (a.n + T::ROWS - 1) / T::ROWS;
   const int total = (int)(a.bh * n_qtiles);
-  return launch_kernel(fwd_f32_kernel<D, CAUSAL, SPARSE>, dim3(total),
+  return launch_kernel(fwd_f32_kernel<D, CAUSAL, SPARSE, KSPLIT>, dim3(total),
                        dim3(256), s, (const float*)a.q, (const float*)a.k,
                        (const float*)a.v, (float*)a.o, a.lse, a.n, n_qtiles,
                        a.scale * kLog2e, a.mask, a.mask_cols, a.block_m,
                        a.block_n);
+}
+
+// Problems with fewer than two workgroups per CU in the plain layout take
+// the key-split layout (four times the workgroups, a quarter of the keys
+// per lane).
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+  using T = F32Tile<D, 1>;
+  const int64_t wgs = a.bh * ((a.n + T::ROWS - 1) / T::ROWS);
+  if (wgs < 2 * kNumCus) return launch_k<D, CAUSAL, SPARSE, 4>(a, s);
+  return launch_k<D, CAUSAL, SPARSE, 1>(a, s);
 }
 
 template <int D>
