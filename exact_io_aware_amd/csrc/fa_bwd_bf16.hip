@@ -143,7 +143,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const float* __restrict__ ws_d,
                      const float* __restrict__ ws_lse2, float* __restrict__ dK,
                      float* __restrict__ dV, int n, int n_ktiles, int total,
-                     float c_log2, float scale, const uint8_t* __restrict__ mask,
+                     int bundle, float c_log2, float scale,
+                     const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n) {
   using T = KVTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
@@ -156,8 +157,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int qh = w >> 2;  // query half of this wave
 
   const int lid = xcd_logical_id(blockIdx.x, total);
-  const int head = lid / n_ktiles;
-  const int k0 = (lid % n_ktiles) * T::BCK;  // early key tiles are the heavy ones
+  // Under the causal rule early key tiles are the heavy ones.
+  const CausalPlace pl = CAUSAL ? causal_place(lid, n_ktiles, total / n_ktiles, bundle)
+                                : CausalPlace{lid / n_ktiles, lid % n_ktiles};
+  const int head = pl.head;
+  const int k0 = pl.rank * T::BCK;
   const int64_t hoff = (int64_t)head * n * D;
   const int64_t roff = (int64_t)head * n;
   const int kw0 = k0 + 32 * kw;
@@ -427,7 +431,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ ws_d,
                    const float* __restrict__ ws_lse2, float* __restrict__ dQ,
-                   int n, int n_qtiles, int total, float c_log2, float scale,
+                   int n, int n_qtiles, int total, int bundle, float c_log2,
+                   float scale,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
                    int block_n) {
   using T = QTile<D, NW>;
@@ -439,8 +444,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int l32 = lane & 31;
 
   const int lid = xcd_logical_id(blockIdx.x, total);
-  const int head = lid / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
+  const CausalPlace pl = CAUSAL ? causal_place(lid, n_qtiles, total / n_qtiles, bundle)
+                                : CausalPlace{lid / n_qtiles, lid % n_qtiles};
+  const int head = pl.head;
+  const int qt = CAUSAL ? (n_qtiles - 1 - pl.rank) : pl.rank;
   const int q0 = qt * T::BRQ;
   const int64_t hoff = (int64_t)head * n * D;
   const bf16* Kh = K + hoff;
@@ -638,8 +645,8 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
-                       a.scale * kLog2e, a.scale, a.mask, a.mask_cols, a.block_m,
-                       a.block_n);
+                       causal_bundle(n_kt, 1), a.scale * kLog2e, a.scale,
+                       a.mask, a.mask_cols, a.block_m, a.block_n);
 }
 
 // d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
@@ -654,8 +661,8 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
-                       a.scale * kLog2e, a.scale, a.mask, a.mask_cols, a.block_m,
-                       a.block_n);
+                       causal_bundle(n_qt, NW == 8 ? 1 : 2), a.scale * kLog2e,
+                       a.scale, a.mask, a.mask_cols, a.block_m, a.block_n);
 }
 
 template <int D, bool SPARSE>

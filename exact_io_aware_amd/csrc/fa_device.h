@@ -187,6 +187,35 @@ __device__ __forceinline__ int xcd_logical_id(int g, int total) {
   return (g % kNumXcd) * per + g / kNumXcd;
 }
 
+// Order of the workgroups of a causal problem, whose tiles of one head
+// carry different amounts of work.  Logical ids (XCD-contiguous, above) run
+// over bundles of `bundle` consecutive heads; inside a bundle they go
+// heaviest tile first across the bundle's heads.  With bundle = 1 this is
+// head by head, heaviest tile first, which keeps one head's K/V hot in an
+// XCD's L2 when its tiles fill the XCD; when a head has fewer tiles than an
+// XCD has workgroup slots, bundle = slots / tiles (rounded up) keeps the
+// longest-first order across the XCD.  Returns the head and the tile's rank
+// (0 = heaviest).
+struct CausalPlace {
+  int head, rank;
+};
+__device__ __forceinline__ CausalPlace causal_place(int lid, int n_tiles,
+                                                    int n_heads, int bundle) {
+  const int per = bundle * n_tiles;
+  const int b = lid / per;
+  const int h0 = b * bundle;
+  const int nb = min(bundle, n_heads - h0);
+  const int idx = lid - b * per;
+  return {h0 + idx % nb, idx / nb};
+}
+
+// Bundle size for causal_place: enough heads to fill the workgroup slots of
+// one XCD (32 CUs times the workgroups that fit on a CU).
+inline int causal_bundle(int n_tiles, int wgs_per_cu) {
+  const int slots = 32 * wgs_per_cu;
+  return n_tiles >= slots ? 1 : (slots + n_tiles - 1) / n_tiles;
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch returning the launch's own status (hipLaunchKernel does
 // not report errors left over from earlier, unrelated calls).

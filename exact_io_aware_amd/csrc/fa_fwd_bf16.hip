@@ -435,10 +435,14 @@ struct FwdPlace {
   int head, q0;
 };
 template <bool CAUSAL>
-__device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br) {
+__device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br,
+                                              int bundle) {
   const int lid = xcd_logical_id(blockIdx.x, total);
-  const int qt = CAUSAL ? (n_qtiles - 1 - lid % n_qtiles) : (lid % n_qtiles);
-  return {lid / n_qtiles, qt * br};
+  if (CAUSAL) {
+    const CausalPlace p = causal_place(lid, n_qtiles, total / n_qtiles, bundle);
+    return {p.head, (n_qtiles - 1 - p.rank) * br};
+  }
+  return {lid / n_qtiles, (lid % n_qtiles) * br};
 }
 
 // With d = 128 (dense) a workgroup has 8 waves, one workgroup per CU: 256
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int n, int n_qtiles, int total,
-                     float c_log2, const uint8_t* __restrict__ mask,
+                     int bundle, float c_log2, const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n) {
   using T = FwdTile<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
@@ -460,7 +464,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR);
+  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR, bundle);
   const int64_t hoff = (int64_t)pl.head * n * D;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
@@ -494,11 +498,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   using T = FwdTile<D, NW>;
   const int n_qtiles = (a.n + T::BR - 1) / T::BR;
   const int total = (int)(a.bh * n_qtiles);
+  const int bundle = causal_bundle(n_qtiles, NW == 8 ? 1 : 2);
   return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
-                       total, a.scale * kLog2e, a.mask, a.mask_cols, a.block_m,
-                       a.block_n);
+                       total, bundle, a.scale * kLog2e, a.mask, a.mask_cols,
+                       a.block_m, a.block_n);
 }
 
 template <int D>
