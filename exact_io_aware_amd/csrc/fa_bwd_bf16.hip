@@ -233,11 +233,16 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   // Block-sparse: the query tiles whose mask block in this workgroup's key
   // column is nonzero (a 64-row tile lies in one 128-multiple block row).
-  const uint8_t* mcol = SPARSE ? mask + k0 / block_n : nullptr;
+  MaskLine mline(SPARSE ? mask + k0 / block_n : mask, mask_cols,
+                 SPARSE ? (n + block_m - 1) / block_m : 0, lane);
   auto next_on = [&](int qt) -> int {
     ++qt;
     if constexpr (SPARSE) {
-      while (qt < n_qt && mcol[(int64_t)((qt * T::BRQ) / block_m) * mask_cols] == 0) ++qt;
+      if (qt < n_qt) {
+        const int row = (qt * T::BRQ) / block_m;
+        const int nr = mline.next(row, lane);
+        if (nr != row) qt = min(n_qt, (int)(((int64_t)nr * block_m) / T::BRQ));
+      }
     }
     return __builtin_amdgcn_readfirstlane(qt);
   };
@@ -519,12 +524,16 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Block-sparse: the key tiles whose mask block in this workgroup's row is
   // nonzero (a workgroup's 128 rows lie in one block row, a key tile in one
   // block column).
-  const uint8_t* mrow =
-      SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
+  MaskLine mline(SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : mask, 1,
+                 SPARSE ? mask_cols : 0, lane);
   auto next_on = [&](int kt) -> int {
     ++kt;
     if constexpr (SPARSE) {
-      while (kt < kt_end && mrow[(kt * T::BCK) / block_n] == 0) ++kt;
+      if (kt < kt_end) {
+        const int col = (kt * T::BCK) / block_n;
+        const int nc = mline.next(col, lane);
+        if (nc != col) kt = min(kt_end, (int)(((int64_t)nc * block_n) / T::BCK));
+      }
     }
     return __builtin_amdgcn_readfirstlane(kt);
   };

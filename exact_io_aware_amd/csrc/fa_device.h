@@ -216,6 +216,40 @@ inline int causal_bundle(int n_tiles, int wgs_per_cu) {
   return n_tiles >= slots ? 1 : (slots + n_tiles - 1) / n_tiles;
 }
 
+// One row (or column) of a block mask, read 64 entries at a time: each
+// lane loads one byte and a ballot turns the window into a 64-bit set held
+// in scalar registers, so finding the next visible block is a bit scan
+// rather than one scalar load per probe (scalar loads share their wait
+// counter with LDS reads, and each probe would wait for those too).
+struct MaskLine {
+  const uint8_t* p;   // entry c is p[c * stride]
+  int64_t stride;
+  int cols, win0;
+  uint64_t bits;      // entries win0 .. win0 + 63 that are nonzero
+
+  __device__ __forceinline__ MaskLine(const uint8_t* p_, int64_t stride_,
+                                      int cols_, int lane)
+      : p(p_), stride(stride_), cols(cols_) {
+    load(0, lane);
+  }
+  __device__ __forceinline__ void load(int w0, int lane) {
+    win0 = w0;
+    const int c = w0 + lane;
+    const bool on = (c < cols) && p[(int64_t)c * stride] != 0;
+    bits = __ballot(on);
+  }
+  // The first nonzero entry at or after c (cols if there is none).
+  __device__ __forceinline__ int next(int c, int lane) {
+    while (c < cols) {
+      if (c >= win0 + 64) load(c & ~63, lane);
+      const uint64_t b = bits >> (c - win0);
+      if (b) return c + __builtin_ctzll(b);
+      c = win0 + 64;
+    }
+    return cols;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Host-side launch returning the launch's own status (hipLaunchKernel does
 // not report errors left over from earlier, unrelated calls).

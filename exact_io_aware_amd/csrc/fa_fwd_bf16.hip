@@ -475,15 +475,21 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int n_ktiles = (n + T::BC - 1) / T::BC;
   int kt_end = n_ktiles;
   if (CAUSAL) kt_end = min(n_ktiles, (min(pl.q0 + T::BR, n) - 1) / T::BC + 1);
-  const uint8_t* mrow =
-      SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : nullptr;
+  // Block-sparse: the mask row of this workgroup's block row (a 64-entry
+  // window at a time).  A key tile lies in one mask column.
+  MaskLine mline(SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : mask,
+                 1, SPARSE ? mask_cols : 0, lane);
   // (readfirstlane keeps the index opaque to induction-variable rewriting,
   // which would otherwise turn every DMA source into a loop-carried 64-bit
   // pointer and exhaust the register file.)
   auto next_on = [&](int kt) -> int {
     ++kt;
     if constexpr (SPARSE) {
-      while (kt < kt_end && mrow[(kt * T::BC) / block_n] == 0) ++kt;
+      if (kt < kt_end) {
+        const int col = (kt * T::BC) / block_n;
+        const int nc = mline.next(col, lane);
+        if (nc != col) kt = min(kt_end, (int)(((int64_t)nc * block_n) / T::BC));
+      }
     }
     return __builtin_amdgcn_readfirstlane(kt);
   };
