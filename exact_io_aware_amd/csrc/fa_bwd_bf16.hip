@@ -157,13 +157,31 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int qh = w >> 2;  // query half of this wave
 
   const int lid = xcd_logical_id(blockIdx.x, total);
-  // Under the causal rule early key tiles are the heavy ones.
-  const CausalPlace pl = CAUSAL ? causal_place(lid, n_ktiles, total / n_ktiles, bundle)
-                                : CausalPlace{lid / n_ktiles, lid % n_ktiles};
-  const int head = pl.head;
-  const int k0 = pl.rank * T::BCK;
+  // Under the causal rule early key tiles are the heavy ones.  Dense causal:
+  // the workgroup takes key tiles u and n_ktiles-1-u of one head, whose
+  // query counts add up to the same total for every u, so that all
+  // workgroups carry equal work (the hardware hands workgroups to CUs in a
+  // fixed rotation, which leaves CUs idle behind longer ones).
+  constexpr bool PAIRS = CAUSAL && !SPARSE;
+  int head, kt_a, kt_b = -1;
+  if constexpr (PAIRS) {
+    const int units = (n_ktiles + 1) / 2;
+    const int u = lid % units;
+    head = lid / units;
+    kt_a = u;
+    if (u != n_ktiles - 1 - u) kt_b = n_ktiles - 1 - u;
+  } else {
+    const CausalPlace pl = CAUSAL ? causal_place(lid, n_ktiles, total / n_ktiles, bundle)
+                                  : CausalPlace{lid / n_ktiles, lid % n_ktiles};
+    head = pl.head;
+    kt_a = pl.rank;
+  }
   const int64_t hoff = (int64_t)head * n * D;
   const int64_t roff = (int64_t)head * n;
+
+  // One key tile of 128 keys.
+  auto run_tile = [&](int kt) {
+  const int k0 = kt * T::BCK;
   const int kw0 = k0 + 32 * kw;
   const int key = kw0 + l32;
 
@@ -403,6 +421,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
     }
   }
+  };
+
+  run_tile(kt_a);
+  if (PAIRS && kt_b >= 0) {
+    __syncthreads();  // the partial sums are read before K/V are refilled
+    run_tile(kt_b);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -449,14 +474,30 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int l32 = lane & 31;
 
   const int lid = xcd_logical_id(blockIdx.x, total);
-  const CausalPlace pl = CAUSAL ? causal_place(lid, n_qtiles, total / n_qtiles, bundle)
-                                : CausalPlace{lid / n_qtiles, lid % n_qtiles};
-  const int head = pl.head;
-  const int qt = CAUSAL ? (n_qtiles - 1 - pl.rank) : pl.rank;
-  const int q0 = qt * T::BRQ;
+  // Dense causal with 256-row tiles: the workgroup takes query tiles
+  // n_qtiles-1-u and u of one head (equal work for every workgroup, see the
+  // forward kernel).
+  constexpr bool PAIRS = CAUSAL && !SPARSE && NW == 8;
+  int head, qt_a, qt_b = -1;
+  if constexpr (PAIRS) {
+    const int units = (n_qtiles + 1) / 2;
+    const int u = lid % units;
+    head = lid / units;
+    qt_a = n_qtiles - 1 - u;
+    if (u != qt_a) qt_b = u;
+  } else {
+    const CausalPlace pl = CAUSAL ? causal_place(lid, n_qtiles, total / n_qtiles, bundle)
+                                  : CausalPlace{lid / n_qtiles, lid % n_qtiles};
+    head = pl.head;
+    qt_a = CAUSAL ? (n_qtiles - 1 - pl.rank) : pl.rank;
+  }
   const int64_t hoff = (int64_t)head * n * D;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
+
+  // One query tile of 32 * NW rows.
+  auto run_tile = [&](int qt) {
+  const int q0 = qt * T::BRQ;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
 
@@ -633,6 +674,13 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
     }
   }
+  };
+
+  run_tile(qt_a);
+  if (PAIRS && qt_b >= 0) {
+    __syncthreads();  // every wave is done with the K/V stages
+    run_tile(qt_b);
+  }
 }
 
 template <int D>
@@ -649,7 +697,9 @@ template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = KVTile<D>;
   const int n_kt = (a.n + T::BCK - 1) / T::BCK;
-  const int total = (int)(a.bh * n_kt);
+  // Dense causal workgroups take two key tiles each (see the kernel).
+  const int units = (CAUSAL && !SPARSE) ? (n_kt + 1) / 2 : n_kt;
+  const int total = (int)(a.bh * units);
   return launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SPARSE>, dim3(total), dim3(512), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
@@ -665,7 +715,9 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = QTile<D, NW>;
   const int n_qt = (a.n + T::BRQ - 1) / T::BRQ;
-  const int total = (int)(a.bh * n_qt);
+  // Dense causal 8-wave workgroups take two tiles each (see the kernel).
+  const int units = (CAUSAL && !SPARSE && NW == 8) ? (n_qt + 1) / 2 : n_qt;
+  const int total = (int)(a.bh * units);
   return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,

@@ -464,38 +464,62 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const FwdPlace pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR, bundle);
+  // Dense causal with 256-row tiles: the workgroup takes query tiles
+  // n_qtiles-1-u and u of one head, whose key counts add up to the same
+  // total for every u, so that all workgroups carry equal work (the
+  // hardware hands workgroups to CUs in a fixed rotation, which leaves CUs
+  // idle behind longer ones).
+  constexpr bool PAIRS = CAUSAL && !SPARSE && NW == 8;
+  FwdPlace pl;
+  int q0_b = -1;  // the second tile's first row, -1 if none
+  if constexpr (PAIRS) {
+    const int units = (n_qtiles + 1) / 2;
+    const int lid = xcd_logical_id(blockIdx.x, total);
+    const int u = lid % units;
+    pl = {lid / units, (n_qtiles - 1 - u) * T::BR};
+    if (u != n_qtiles - 1 - u) q0_b = u * T::BR;
+  } else {
+    pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR, bundle);
+  }
   const int64_t hoff = (int64_t)pl.head * n * D;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
   const TileFill<T> fill(w, lane);
-  FwdWave<T, CAUSAL> wv(Q + hoff, pl.q0 + 32 * w, lane, n, n, 0, c_log2);
-
-  // Key tiles to visit, in order.
   const int n_ktiles = (n + T::BC - 1) / T::BC;
-  int kt_end = n_ktiles;
-  if (CAUSAL) kt_end = min(n_ktiles, (min(pl.q0 + T::BR, n) - 1) / T::BC + 1);
-  // Block-sparse: the mask row of this workgroup's block row (a 64-entry
-  // window at a time).  A key tile lies in one mask column.
-  MaskLine mline(SPARSE ? mask + (int64_t)(pl.q0 / block_m) * mask_cols : mask,
-                 1, SPARSE ? mask_cols : 0, lane);
-  // (readfirstlane keeps the index opaque to induction-variable rewriting,
-  // which would otherwise turn every DMA source into a loop-carried 64-bit
-  // pointer and exhaust the register file.)
-  auto next_on = [&](int kt) -> int {
-    ++kt;
-    if constexpr (SPARSE) {
-      if (kt < kt_end) {
-        const int col = (kt * T::BC) / block_n;
-        const int nc = mline.next(col, lane);
-        if (nc != col) kt = min(kt_end, (int)(((int64_t)nc * block_n) / T::BC));
+
+  // One query tile of 32 * NW rows from row q0.
+  auto run_tile = [&](int q0) {
+    FwdWave<T, CAUSAL> wv(Q + hoff, q0 + 32 * w, lane, n, n, 0, c_log2);
+    // Key tiles to visit, in order.
+    int kt_end = n_ktiles;
+    if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::BR, n) - 1) / T::BC + 1);
+    // Block-sparse: the mask row of this workgroup's block row (a 64-entry
+    // window at a time).  A key tile lies in one mask column.
+    MaskLine mline(SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : mask,
+                   1, SPARSE ? mask_cols : 0, lane);
+    // (readfirstlane keeps the index opaque to induction-variable rewriting,
+    // which would otherwise turn every DMA source into a loop-carried 64-bit
+    // pointer and exhaust the register file.)
+    auto next_on = [&](int kt) -> int {
+      ++kt;
+      if constexpr (SPARSE) {
+        if (kt < kt_end) {
+          const int col = (kt * T::BC) / block_n;
+          const int nc = mline.next(col, lane);
+          if (nc != col) kt = min(kt_end, (int)(((int64_t)nc * block_n) / T::BC));
+        }
       }
-    }
-    return __builtin_amdgcn_readfirstlane(kt);
+      return __builtin_amdgcn_readfirstlane(kt);
+    };
+    key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on);
+    wv.store(O + hoff, LSE + (int64_t)pl.head * n);
   };
 
-  key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on);
-  wv.store(O + hoff, LSE + (int64_t)pl.head * n);
+  run_tile(pl.q0);
+  if (PAIRS && q0_b >= 0) {
+    __syncthreads();  // every wave is done with the K/V buffers
+    run_tile(q0_b);
+  }
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -503,7 +527,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = FwdTile<D, NW>;
   const int n_qtiles = (a.n + T::BR - 1) / T::BR;
-  const int total = (int)(a.bh * n_qtiles);
+  // Dense causal 8-wave workgroups take two tiles each (see the kernel).
+  const int units = (CAUSAL && !SPARSE && NW == 8) ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int total = (int)(a.bh * units);
   const int bundle = causal_bundle(n_qtiles, NW == 8 ? 1 : 2);
   return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
