@@ -160,7 +160,7 @@ def test_fp32_blocksparse_with_empty_row(dev):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 64, 128, 200, 384, 1000])
+@pytest.mark.parametrize("N", [1, 64, 128, 200, 384, 600, 1000])
 def test_bf16_fwd_shapes(dev, N, d, causal):
     x = gen(2, 3, N, d, seed=200 + N + d, dev=dev)
     scale = 1 / math.sqrt(d)
