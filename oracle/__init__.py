@@ -17,3 +17,11 @@ from .attention import (  # noqa: F401
     tiled_fwd_head,
     visible,
 )
+from .dropout import (  # noqa: F401,E402
+    attention_bwd_dropout_head,
+    attention_fwd_dropout_head,
+    dropout_bytes,
+    dropout_keep,
+    dropout_threshold,
+    philox4x32_10,
+)

@@ -13,7 +13,7 @@ import types
 
 import pytest
 
-from tests import oracle_pins
+from tests import oracle_pins, oracle_pins_dropout
 
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle",
                         "attention.py")
@@ -100,5 +100,70 @@ def test_mutant_is_caught(desc, old, new, occ):
         try:
             check(mod)
         except Exception:       # AssertionError, or a crash on bad shapes
+            return
+    pytest.fail(f"no pin catches the planted mistake: {desc}")
+
+
+DROPOUT_SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(__file__)),
+                                "oracle", "dropout.py")
+
+# Planted mistakes in the dropout oracle (same scheme).
+DROPOUT_MUTATIONS = [
+    ("philox: multipliers swapped", "p0 = x0 * np.uint64(_M0)",
+     "p0 = x0 * np.uint64(_M1)", 0),
+    ("philox: key not advanced", "k0 = (k0 + _W0) & _MASK32", "k0 = k0", 0),
+    ("philox: permutation slip", "x1 = lo1", "x1 = lo0", 0),
+    ("philox: nine rounds", "for _ in range(10):", "for _ in range(9):", 0),
+    ("philox: key words swapped", "x0 = hi1 ^ x1 ^ np.uint64(k0)",
+     "x0 = hi1 ^ x1 ^ np.uint64(k1)", 0),
+    ("mapping: row and column blocks swapped",
+     "ctr = np.stack([R, C, np.full_like(R, bh)",
+     "ctr = np.stack([C, R, np.full_like(R, bh)", 0),
+    ("mapping: word from the column", "(rows & 3)[:, None]]",
+     "(cols & 3)[None, :]]", 0),
+    ("mapping: byte from the row", "shift = (8 * (cols & 3))",
+     "shift = (8 * (rows[:1] & 3))", 0),
+    ("mapping: seed halves swapped",
+     "(seed & _MASK32, (seed >> 32) & _MASK32)",
+     "((seed >> 32) & _MASK32, seed & _MASK32)", 0),
+    ("keep: strict comparison", "seed) >= t", "seed) > t", 0),
+    ("threshold: truncated", "t = int(np.rint(256.0 * float(p)))",
+     "t = int(256.0 * float(p))", 0),
+    ("fwd: survivors not rescaled", "Pd = np.where(Z, P, 0.0) * (256.0 / (256.0 - t))",
+     "Pd = np.where(Z, P, 0.0)", 0),
+    ("fwd: LSE of the dropped row", "m + np.log(l))",
+     "m + np.log((Pd * l[:, None]).sum(axis=1)))", 0),
+    ("bwd: dP not masked", "dP = np.where(Z, dPd, 0.0) * c", "dP = dPd", 0),
+    ("bwd: dP not rescaled", "dP = np.where(Z, dPd, 0.0) * c",
+     "dP = np.where(Z, dPd, 0.0)", 0),
+    ("bwd: dV from the undropped P", "dv = Pd.T @ do", "dv = P.T @ do", 0),
+    ("bwd: D from the dropped P", "D = (P * dP).sum(axis=1)",
+     "D = (Pd * dP).sum(axis=1)", 0),
+]
+
+
+def _dropout_mutant(old, new, occurrence):
+    with open(DROPOUT_SRC_PATH) as f:
+        src = f.read()
+    parts = src.split(old)
+    assert len(parts) - 1 > occurrence, f"pattern not in oracle: {old!r}"
+    mutated = old.join(parts[:occurrence + 1]) + new + old.join(
+        parts[occurrence + 1:])
+    assert mutated != src
+    # run outside the package: the relative import names the real module
+    mutated = mutated.replace("from .attention import", "from oracle.attention import")
+    mod = types.ModuleType("oracle_dropout_mutant")
+    exec(compile(mutated, "<dropout oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("desc,old,new,occ", DROPOUT_MUTATIONS,
+                         ids=[m[0] for m in DROPOUT_MUTATIONS])
+def test_dropout_mutant_is_caught(desc, old, new, occ):
+    mod = _dropout_mutant(old, new, occ)
+    for check in oracle_pins_dropout.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:
             return
     pytest.fail(f"no pin catches the planted mistake: {desc}")
