@@ -193,11 +193,16 @@ def time_passes(name, steps, warmup):
         torch.cuda.synchronize()
         return sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
 
+    p_drop = w.get("p_drop", 0.0)
     for causal in w["causal"]:
         def fwd():
             if mask_t is not None:
                 return fa.fa_fwd_blocksparse(x["q"], x["k"], x["v"], mask_t,
                                              scale=w["scale"], causal=causal)
+            if p_drop:
+                return fa.fa_fwd_dropout(x["q"], x["k"], x["v"], p_drop,
+                                         w["drop_seed"], scale=w["scale"],
+                                         causal=causal)
             return fa.fa_fwd(x["q"], x["k"], x["v"], scale=w["scale"],
                              causal=causal)
         if mask is not None:
@@ -220,14 +225,20 @@ def time_passes(name, steps, warmup):
                 if mask_t is not None:
                     fa.fa_bwd_blocksparse(x["q"], x["k"], x["v"], o, x["do"],
                                           lse, mask_t, **kw)
+                elif p_drop:
+                    fa.fa_bwd_dropout(x["q"], x["k"], x["v"], o, x["do"], lse,
+                                      p_drop, w["drop_seed"], **kw)
                 else:
                     fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, **kw)
             passes.append(("bwd", bwd, 2.5 * flops))
         for pname, run, fl in passes:
             ms = median_ms(run)
             tf = fl / (ms * 1e-3) / 1e12
-            out.append(dict(workload=name, causal=causal, pass_=pname,
-                            ms_median=ms, tflops=tf, frac_peak=tf / peak))
+            res = dict(workload=name, causal=causal, pass_=pname,
+                       ms_median=ms, tflops=tf, frac_peak=tf / peak)
+            if p_drop:
+                res["p_drop"] = p_drop
+            out.append(res)
     return out
 
 

@@ -54,11 +54,21 @@ size_t ws_bytes(int64_t bh, int64_t n) { return 2 * ws_rows(bh, n) * 4; }
 
 fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout threshold t = round(256 p) (drop probability t / 256); valid for a
+// finite p >= 0 with t <= 255.
+bool dropout_t(float p, int* t) {
+  if (!isfinite(p) || p < 0.f || p > 1.f) return false;
+  const long r = lrintf(p * 256.f);
+  if (r > 255) return false;
+  *t = (int)r;
+  return true;
+}
+
 fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
                      float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
                      fa_dtype dt, float scale, int causal, const uint8_t* mask,
                      int64_t block_m, int64_t block_n, bool sparse_call,
-                     void* stream) {
+                     void* stream, int drop_t = 0, uint64_t seed = 0) {
   bool empty = false;
   int64_t bh = 0;
   fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
@@ -91,6 +101,9 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
   a.block_m = (int)(sparse_call ? block_m : 128);
   a.block_n = (int)(sparse_call ? block_n : 128);
   a.mask_cols = (int)((N + a.block_n - 1) / a.block_n);
+  a.drop_t = drop_t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return from_hip(dt == FA_BF16 ? fa::launch_fwd_bf16(a, s)
                                 : fa::launch_fwd_f32(a, s));
@@ -294,6 +307,21 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
                     block_m, block_n, true, stream);
 }
 
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t N,
+                         int64_t d, fa_dtype dt, float scale, int causal,
+                         float p_drop, uint64_t seed, void* stream) {
+  bool empty = false;
+  int64_t bh = 0;
+  fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
+  if (st != FA_OK) return st;
+  int t = 0;
+  if (!scale_ok(scale) || !dropout_t(p_drop, &t)) return FA_ERR_ARG;
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  return fwd_common(q, k, v, o, lse, B, H, N, d, dt, scale, causal, nullptr,
+                    128, 128, false, stream, t, seed);
+}
+
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   bool empty = false;
   int64_t bh = 0;
@@ -364,6 +392,34 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   return from_hip(run_dq(a, dt, s));
 }
 
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t N, int64_t d, fa_dtype dt, float scale,
+                         int causal, float p_drop, uint64_t seed,
+                         void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty);
+  if (st != FA_OK) return st;
+  int t = 0;
+  if (!dropout_t(p_drop, &t)) return FA_ERR_ARG;
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  a.drop_t = t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(run_pre(a, dt, s));
+  if (st != FA_OK) return st;
+  st = from_hip(run_dkdv(a, dt, s));
+  if (st != FA_OK) return st;
+  return from_hip(run_dq(a, dt, s));
+}
+
 fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse,
                              float* dq, float* dk, float* dv, void* workspace,
@@ -399,7 +455,8 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointer not 16-byte aligned";
     case FA_ERR_ARG:
-      return "FA_ERR_ARG: scale must be finite and > 0, workspace large enough";
+      return "FA_ERR_ARG: scale must be finite and > 0, workspace large enough, "
+             "drop probability in [0, 255/256]";
   }
   return "unknown fa_status";
 }

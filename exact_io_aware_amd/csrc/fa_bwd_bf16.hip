@@ -136,7 +136,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int toff[DB][2]) {
 // operands), which keeps the per-wave register footprint within the 256
 // registers that two waves per SIMD allow.  Query tiles are double-buffered
 // and filled by direct global-to-LDS loads.
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
@@ -145,7 +145,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ dV, int n, int n_ktiles, int total,
                      int bundle, float c_log2, float scale,
                      const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n) {
+                     int mask_cols, int block_m, int block_n, Dropout drop) {
   using T = KVTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
 
@@ -178,6 +178,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   const int64_t hoff = (int64_t)head * n * D;
   const int64_t roff = (int64_t)head * n;
+  drop.bh = (uint32_t)head;
 
   // One key tile of 128 keys.
   auto run_tile = [&](int kt) {
@@ -286,6 +287,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       const int qb = qh * T::QBW + qi;
       const int qq0 = qt * T::BRQ + qb * 32;
       if (MASK && CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
+      // Dropout: dV takes the kept probabilities (the 1/(1-p) factor is
+      // applied at the end), dS the kept and rescaled dP.
+      uint32_t u[4];
+      if constexpr (DROP) dropout_bytes_keylane(drop, key, qq0, lane, u);
       // S = Q K^T and dP = dO V^T (M = query, N = key), both operands from LDS.
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -313,8 +318,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             const int qr = g * 8 + t;
             if (qr < qlo || qr >= qhi) p = 0.f;
           }
-          s[i] = p;
-          dp[i] = p * (dp[i] - Dv[t]);
+          if constexpr (DROP) {
+            const bool keep = dropout_keep(u[g], t, drop.t);
+            s[i] = keep ? p : 0.f;
+            dp[i] = p * ((keep ? dp[i] * drop.inv_keep : 0.f) - Dv[t]);
+          } else {
+            s[i] = p;
+            dp[i] = p * (dp[i] - Dv[t]);
+          }
         }
       }
       const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
@@ -415,6 +426,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int t = 0; t < 4; ++t) {
           xk[t] = (adk[db][4 * g + t] + red[slot(0, db, 4 * g + t)]) * scale;
           xv[t] = adv[db][4 * g + t] + red[slot(1, db, 4 * g + t)];
+          if constexpr (DROP) xv[t] *= drop.inv_keep;
         }
         *reinterpret_cast<f32x4*>(dkr + c) = xk;
         *reinterpret_cast<f32x4*>(dvr + c) = xv;
@@ -455,7 +467,7 @@ struct QTile {
 // has 4 waves and two run per CU.  Wave w owns queries q0 + 32w .. + 31; Q
 // and dO stay in registers as B operands.  K/V tiles are double-buffered
 // and filled by direct global-to-LDS loads one tile ahead.
-template <int D, int NW, bool CAUSAL, bool SPARSE>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
@@ -464,7 +476,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    int n, int n_qtiles, int total, int bundle, float c_log2,
                    float scale,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
-                   int block_n) {
+                   int block_n, Dropout drop) {
   using T = QTile<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
 
@@ -494,6 +506,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int64_t hoff = (int64_t)head * n * D;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
+  drop.bh = (uint32_t)head;
 
   // One query tile of 32 * NW rows.
   auto run_tile = [&](int qt) {
@@ -601,13 +614,19 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
       }
+      // Dropout: dS takes the kept and rescaled dP.
+      uint32_t u[4];
+      if constexpr (DROP) dropout_bytes_rowlane(drop, qrow, kbase + kb * 32, lane, u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
         if constexpr (MASK) {
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) p = 0.f;
         }
-        dp[i] = p * (dp[i] - drow);
+        float dpv = dp[i];
+        if constexpr (DROP)
+          dpv = dropout_keep(u[i >> 2], i & 3, drop.t) ? dpv * drop.inv_keep : 0.f;
+        dp[i] = p * (dpv - drow);
       }
       const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
       // dQ^T += K^T dS^T (M = d, N = query, K = key); K^T from transpose
@@ -693,24 +712,25 @@ hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
                        a.ws_lse2, rows);
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = KVTile<D>;
   const int n_kt = (a.n + T::BCK - 1) / T::BCK;
   // Dense causal workgroups take two key tiles each (see the kernel).
   const int units = (CAUSAL && !SPARSE) ? (n_kt + 1) / 2 : n_kt;
   const int total = (int)(a.bh * units);
-  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SPARSE>, dim3(total), dim3(512), s,
+  return launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SPARSE, DROP>, dim3(total), dim3(512), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
                        causal_bundle(n_kt, 1), a.scale * kLog2e, a.scale,
-                       a.mask, a.mask_cols, a.block_m, a.block_n);
+                       a.mask, a.mask_cols, a.block_m, a.block_n,
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
 }
 
 // d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
 // rows so that a workgroup lies in one 128-multiple block row of the mask.
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = QTile<D, NW>;
@@ -718,21 +738,35 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   // Dense causal 8-wave workgroups take two tiles each (see the kernel).
   const int units = (CAUSAL && !SPARSE && NW == 8) ? (n_qt + 1) / 2 : n_qt;
   const int total = (int)(a.bh * units);
-  return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
+  return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE, DROP>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,
                        (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
                        causal_bundle(n_qt, NW == 8 ? 1 : 2), a.scale * kLog2e,
-                       a.scale, a.mask, a.mask_cols, a.block_m, a.block_n);
+                       a.scale, a.mask, a.mask_cols, a.block_m, a.block_n,
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
 }
 
-template <int D, bool SPARSE>
+// Block-sparse, dropout (dense only) or neither.
+template <int D>
 hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
-  return a.causal ? dkdv_t<D, true, SPARSE>(a, s) : dkdv_t<D, false, SPARSE>(a, s);
+  if (a.mask) {
+    return a.causal ? dkdv_t<D, true, true, false>(a, s) : dkdv_t<D, false, true, false>(a, s);
+  }
+  if (a.drop_t > 0) {
+    return a.causal ? dkdv_t<D, true, false, true>(a, s) : dkdv_t<D, false, false, true>(a, s);
+  }
+  return a.causal ? dkdv_t<D, true, false, false>(a, s) : dkdv_t<D, false, false, false>(a, s);
 }
-template <int D, bool SPARSE>
+template <int D>
 hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
-  return a.causal ? dq_t<D, true, SPARSE>(a, s) : dq_t<D, false, SPARSE>(a, s);
+  if (a.mask) {
+    return a.causal ? dq_t<D, true, true, false>(a, s) : dq_t<D, false, true, false>(a, s);
+  }
+  if (a.drop_t > 0) {
+    return a.causal ? dq_t<D, true, false, true>(a, s) : dq_t<D, false, false, true>(a, s);
+  }
+  return a.causal ? dq_t<D, true, false, false>(a, s) : dq_t<D, false, false, false>(a, s);
 }
 
 }  // namespace
@@ -742,13 +776,11 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
-  if (a.mask) return a.d == 128 ? dkdv_c<128, true>(a, s) : dkdv_c<64, true>(a, s);
-  return a.d == 128 ? dkdv_c<128, false>(a, s) : dkdv_c<64, false>(a, s);
+  return a.d == 128 ? dkdv_c<128>(a, s) : dkdv_c<64>(a, s);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.mask) return a.d == 128 ? dq_c<128, true>(a, s) : dq_c<64, true>(a, s);
-  return a.d == 128 ? dq_c<128, false>(a, s) : dq_c<64, false>(a, s);
+  return a.d == 128 ? dq_c<128>(a, s) : dq_c<64>(a, s);
 }
 
 }  // namespace fa

@@ -216,6 +216,118 @@ inline int causal_bundle(int n_tiles, int wgs_per_cu) {
   return n_tiles >= slots ? 1 : (slots + n_tiles - 1) / n_tiles;
 }
 
+// ---------------------------------------------------------------------------
+// Dropout on the attention probabilities ([XYZ] key ideas: dropout is one of
+// the steps fused into the attention kernel).  The random numbers come from
+// the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).  Element (bh, i,
+// j) of head bh, query i and key j takes byte (j & 3) of word (i & 3) of the
+// call with counter (i >> 2, j >> 2, bh, 0) and key (seed low, seed high);
+// it is kept iff that byte is >= t (drop probability t / 256).  One call
+// covers a 4 x 4 block of scores, so the mask does not depend on the tiling.
+// ---------------------------------------------------------------------------
+struct Dropout {
+  uint32_t k0, k1;  // seed words
+  uint32_t bh;      // head index b * H + h
+  uint32_t t;       // keep iff byte >= t
+  float inv_keep;   // 256 / (256 - t)
+};
+
+inline Dropout make_dropout(int t, uint32_t seed_lo, uint32_t seed_hi) {
+  return Dropout{seed_lo, seed_hi, 0u, (uint32_t)t, 256.f / (float)(256 - t)};
+}
+
+// One Philox4x32-10 call: ten rounds of two 32 x 32 -> 64-bit products with
+// the published multipliers and a word permutation, the key advancing by the
+// published Weyl increments after each round.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&x)[4], uint32_t k0,
+                                              uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)x[0] * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)x[2] * 0xCD9E8D57u;
+    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x[1] ^ k0;
+    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x[3] ^ k1;
+    x[0] = y0;
+    x[1] = (uint32_t)p1;
+    x[2] = y2;
+    x[3] = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Transpose of a 4 x 4 matrix of words held by a quad of lanes (lanes 4m ..
+// 4m+3, word index w): afterwards lane q holds in w[g] what lane g held in
+// w[q].  Two stages of lane exchanges within the quad (DPP quad
+// permutations): transpose each 2 x 2 block, then swap the off-diagonal
+// blocks.
+__device__ __forceinline__ void quad_transpose(uint32_t (&w)[4], int lane) {
+  const bool odd = lane & 1, upper = lane & 2;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t send = odd ? w[2 * b] : w[2 * b + 1];
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    if (odd) w[2 * b] = r; else w[2 * b + 1] = r;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t send = upper ? w[b] : w[2 + b];
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);
+    if (upper) w[b] = r; else w[2 + b] = r;
+  }
+}
+
+// Random bytes for the score registers of one 32 x 32 MFMA block in the
+// layout with lane = query row (register r of the block holds key
+// 8 (r / 4) + 4 h + r % 4 relative to key0, h = lane / 32): word g of the
+// result holds, in byte t, the byte of key key0 + 8 g + 4 h + t.  row is this
+// lane's query; key0 is a multiple of 32, rows 4m .. 4m + 3 sit in the lanes
+// of one quad.
+__device__ __forceinline__ void dropout_bytes_rowlane(const Dropout& dr, int row,
+                                                      int key0, int lane,
+                                                      uint32_t (&out)[4]) {
+  const int h = (lane >> 5) & 1, q = lane & 3;
+  // this lane draws the 4 x 4 block of keys key0 + 8 q + 4 h ...
+  out[0] = (uint32_t)row >> 2;
+  out[1] = (uint32_t)(key0 + 8 * q + 4 * h) >> 2;
+  out[2] = dr.bh;
+  out[3] = 0;
+  philox4x32_10(out, dr.k0, dr.k1);
+  // ... whose word q' belongs to row 4 (row >> 2) + q', the lane q' of the quad
+  quad_transpose(out, lane);
+}
+
+// The same in the layout with lane = key (register r of the block holds
+// query 8 (r / 4) + 4 h + r % 4 relative to row0): word g of the result
+// holds, in byte t, the byte of query row0 + 8 g + 4 h + t and this lane's
+// key.  key is this lane's key; keys 4m .. 4m + 3 sit in one quad.
+__device__ __forceinline__ void dropout_bytes_keylane(const Dropout& dr, int key,
+                                                      int row0, int lane,
+                                                      uint32_t (&out)[4]) {
+  const int h = (lane >> 5) & 1, q = lane & 3;
+  uint32_t x[4] = {(uint32_t)(row0 + 8 * q + 4 * h) >> 2, (uint32_t)key >> 2,
+                   dr.bh, 0};
+  philox4x32_10(x, dr.k0, dr.k1);
+  // word u of x belongs to query row0 + 8 q + 4 h + u and holds the four
+  // keys of the quad in its bytes; regroup so that word c holds key c's
+  // bytes of the four queries (byte u = query u) ...
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int sh = 8 * c;
+    out[c] = ((x[0] >> sh) & 0xFFu) | (((x[1] >> sh) & 0xFFu) << 8) |
+             (((x[2] >> sh) & 0xFFu) << 16) | (((x[3] >> sh) & 0xFFu) << 24);
+  }
+  // ... and hand word c to the lane of key c
+  quad_transpose(out, lane);
+}
+
+// Keep test of byte t of a word.
+__device__ __forceinline__ bool dropout_keep(uint32_t word, int t, uint32_t thr) {
+  return ((word >> (8 * t)) & 0xFFu) >= thr;
+}
+
+
 // One row (or column) of a block mask, read 64 entries at a time: each
 // lane loads one byte and a ballot turns the window into a 64-bit set held
 // in scalar registers, so finding the next visible block is a bit scan

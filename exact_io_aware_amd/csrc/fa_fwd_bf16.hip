@@ -148,7 +148,7 @@ struct TileFill {
 // The per-wave part of the forward: 32 query rows, their Q fragments, the
 // output accumulator and the online-softmax state ([TLDR] online softmax;
 // [REAPER] 3.3), and the matrix-core and vector steps on one key tile.
-template <class T, bool CAUSAL>
+template <class T, bool CAUSAL, bool DROP = false>
 struct FwdWave {
   static constexpr int D = T::D;
   bf16x8 qf[T::KS];    // Q as the B operand of S^T = K Q^T
@@ -165,6 +165,7 @@ struct FwdWave {
   // sequence (the causal rule is key <= q_off + row).
   int qw0, qrow, h, n, nk, q_off;
   float c_log2;
+  Dropout dr;          // used when DROP
 
   __device__ __forceinline__ FwdWave(const bf16* Qh, int qw0_, int lane, int n_,
                                      int nk_, int q_off_, float c_log2_)
@@ -261,16 +262,26 @@ struct FwdWave {
     m_use = m_use_new;
   }
   // Probabilities exp2(S*c - m) into the B-operand layout of the PV product
-  // (bf16), and their fp32 row sum into l.
-  __device__ __forceinline__ void probs(f32x16 (&s)[T::KB],
-                                        bf16x8 (&pf)[T::KK]) {
+  // (bf16), and their fp32 row sum into l.  With dropout the row sum keeps
+  // every probability (the softmax statistics are those of P) while the
+  // PV operand has the dropped ones zeroed; the 1/(1-p) factor is applied
+  // with the final division.  kbase: the tile's first key.
+  __device__ __forceinline__ void probs(f32x16 (&s)[T::KB], bf16x8 (&pf)[T::KK],
+                                        int kbase) {
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
+      uint32_t u[4];
+      if constexpr (DROP)
+        dropout_bytes_rowlane(dr, q_off + qrow, kbase + kb * 32, __lane_id(), u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[kb][i] = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
-        rs += s[kb][i];
+        const float p = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
+        rs += p;
+        if constexpr (DROP)
+          s[kb][i] = dropout_keep(u[i >> 2], i & 3, dr.t) ? p : 0.f;
+        else
+          s[kb][i] = p;
       }
       pf[2 * kb] = pack8(s[kb], 0);
       pf[2 * kb + 1] = pack8(s[kb], 1);
@@ -295,7 +306,8 @@ struct FwdWave {
   // LSE = m + ln l in natural-log units.
   __device__ __forceinline__ void store(bf16* Oh, float* lse_h) const {
     const float l_tot = sum_halves(l);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if constexpr (DROP) inv *= dr.inv_keep;
     if (qrow >= n) return;
     bf16* orow = Oh + (int64_t)qrow * D;
 #pragma unroll
@@ -342,8 +354,8 @@ struct FwdWave {
 //            units form tile `cur`'s probabilities;
 //   block B: tile `cur`'s PV product on the matrix cores while the vector
 //            units mask and reduce tile `nxt`'s scores.
-template <class T, bool CAUSAL, class NextOn>
-__device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL>& wv,
+template <class T, bool CAUSAL, bool DROP, class NextOn>
+__device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
                                          const TileFill<T>& fill,
                                          unsigned char* kbuf, unsigned char* vbuf,
                                          const bf16* Kh, const bf16* Vh,
@@ -388,7 +400,7 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL>& wv,
       }
       if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
       bf16x8 pf[T::KK];
-      wv.probs(s, pf);
+      wv.probs(s, pf, cur * T::BC);
       wv.pv(vbuf + kb_cur * T::K_BYTES, pf);
       if constexpr (NEXT) {
         if constexpr (MASK_NEXT) wv.apply_mask(s_next, nxt * T::BC);
@@ -450,14 +462,16 @@ __device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br,
 // Otherwise a workgroup has 4 waves and two run per CU; the block-sparse
 // kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
 // row of the mask.
-template <int D, int NW, bool CAUSAL, bool SPARSE>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int n, int n_qtiles, int total,
                      int bundle, float c_log2, const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n) {
-  using T = FwdTile<D, NW>;
+                     int mask_cols, int block_m, int block_n, Dropout drop) {
+  // (With dropout at d = 64 the key tile is 64 wide, as at d = 128: the
+  // random bytes need registers that 128-key score tiles leave no room for.)
+  using T = FwdTile<D, NW, (D == 128 || DROP) ? 64 : 128>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::K_BYTES];
   unsigned char* const kbuf = smem;                  // K0 | K1
   unsigned char* const vbuf = smem + 2 * T::K_BYTES;  // V0 | V1
@@ -489,7 +503,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   // One query tile of 32 * NW rows from row q0.
   auto run_tile = [&](int q0) {
-    FwdWave<T, CAUSAL> wv(Q + hoff, q0 + 32 * w, lane, n, n, 0, c_log2);
+    FwdWave<T, CAUSAL, DROP> wv(Q + hoff, q0 + 32 * w, lane, n, n, 0, c_log2);
+    if constexpr (DROP) {
+      wv.dr = drop;
+      wv.dr.bh = (uint32_t)pl.head;
+    }
     // Key tiles to visit, in order.
     int kt_end = n_ktiles;
     if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::BR, n) - 1) / T::BC + 1);
@@ -522,7 +540,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = FwdTile<D, NW>;
@@ -531,21 +549,25 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int units = (CAUSAL && !SPARSE && NW == 8) ? (n_qtiles + 1) / 2 : n_qtiles;
   const int total = (int)(a.bh * units);
   const int bundle = causal_bundle(n_qtiles, NW == 8 ? 1 : 2);
-  return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>, dim3(total),
+  return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, DROP>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
                        total, bundle, a.scale * kLog2e, a.mask, a.mask_cols,
-                       a.block_m, a.block_n);
+                       a.block_m, a.block_n, make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
 }
 
 template <int D>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
-  if (a.mask) {
-    return a.causal ? launch_fwd<D, true, true>(a, s)
-                    : launch_fwd<D, false, true>(a, s);
+  if (a.mask) {  // (no dropout with a block mask)
+    return a.causal ? launch_fwd<D, true, true, false>(a, s)
+                    : launch_fwd<D, false, true, false>(a, s);
   }
-  return a.causal ? launch_fwd<D, true, false>(a, s)
-                  : launch_fwd<D, false, false>(a, s);
+  if (a.drop_t > 0) {
+    return a.causal ? launch_fwd<D, true, false, true>(a, s)
+                    : launch_fwd<D, false, false, true>(a, s);
+  }
+  return a.causal ? launch_fwd<D, true, false, false>(a, s)
+                  : launch_fwd<D, false, false, false>(a, s);
 }
 
 // Split-KV forward for a short block of queries against a long key

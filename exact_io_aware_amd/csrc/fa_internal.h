@@ -23,6 +23,9 @@ struct FwdArgs {
   int mask_cols;           // ceil(n / block_n)
   int block_m;             // multiple of 128
   int block_n;             // multiple of 128
+  int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
+  uint32_t seed_lo = 0;    // dropout seed words
+  uint32_t seed_hi = 0;
 };
 
 struct BwdArgs {
@@ -46,6 +49,9 @@ struct BwdArgs {
   int mask_cols;           // ceil(n / block_n)
   int block_m;             // multiple of 128
   int block_n;             // multiple of 128
+  int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
+  uint32_t seed_lo = 0;    // dropout seed words
+  uint32_t seed_hi = 0;
 };
 
 // Split-KV forward: nq queries (the last nq of the nk positions) against nk

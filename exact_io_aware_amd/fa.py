@@ -48,8 +48,8 @@ def library():
             f"HIP attention library not built ({LIB_PATH} missing); run "
             "__graft_entry__.build() first. There is no fallback path.")
     lib = ctypes.CDLL(LIB_PATH)
-    P, I64, F, I, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
-                        ctypes.c_int, ctypes.c_size_t)
+    P, I64, F, I, SZ, U64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64)
     sigs = {
         "fa_fwd": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P],
         "fa_fwd_blocksparse": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
@@ -64,6 +64,10 @@ def library():
         "fa_bwd_dkdv": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I,
                         P],
         "fa_bwd_dq": [P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I, P],
+        "fa_fwd_dropout": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, F, U64,
+                           P],
+        "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
+                           I64, I, F, I, F, U64, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -298,6 +302,42 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
                           ws_bytes, B, H, N, d, _dtype_code(q),
                           _scale(scale, d), int(bool(causal)),
                           _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_fwd_dropout(q, k, v, p_drop, seed, scale=None, causal=False, out=None,
+                   lse=None):
+    """O, LSE of attention with dropout on P (bf16 q, k, v): elements are
+    dropped with probability round(256 p_drop) / 256 by the Philox mask of
+    ``seed`` (a 64-bit integer) and survivors scaled by 1/(1-p); LSE is that
+    of the undropped softmax."""
+    B, H, N, d = _shape4(q, k, v)
+    lib = library()
+    o, lse_t = _fwd_outputs(q, (B, H, N, d), out, lse)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse_t), B, H, N, d, _dtype_code(q),
+                                  _scale(scale, d), int(bool(causal)),
+                                  float(p_drop), int(seed) & (2**64 - 1),
+                                  _stream(q.device)))
+    return o, lse_t
+
+
+def fa_bwd_dropout(q, k, v, o, do, lse, p_drop, seed, scale=None,
+                   causal=False, workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV (float32) of fa_fwd_dropout with the same p_drop and seed."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    lib = library()
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    dq, dk, dv = _grads(q, dq, dk, dv)
+    ws, ws_bytes = _workspace(B, H, N, d, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(ws), ws_bytes, B, H, N, d,
+                                  _dtype_code(q), _scale(scale, d),
+                                  int(bool(causal)), float(p_drop),
+                                  int(seed) & (2**64 - 1), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -82,6 +82,11 @@ DECODE_WORKLOADS = {
 CONTEXT_WORKLOADS = {
     "fp32_1x1x2048x64": _w("fp32_1x1x2048x64", 1, 1, 2048, 64, "f32",
                            (False,), ("fwd",), seed=7),
+    # The metric shape with dropout on P (drop probability 0.1, a typical
+    # training value; the pages give none), to price the fused dropout.
+    "dropout_2x32x8192x128": dict(
+        _w("dropout_2x32x8192x128", 2, 32, 8192, 128, "bf16", (True,),
+           ("fwd", "bwd"), seed=3, sigma=0.5), p_drop=0.1, drop_seed=2024),
 }
 
 

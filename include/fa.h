@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_MASK = 5,        /* block-mask geometry invalid                    */
   FA_ERR_HIP = 6,         /* a HIP launch failed                            */
   FA_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned        */
-  FA_ERR_ARG = 8,         /* scale not finite and > 0, workspace too small  */
+  FA_ERR_ARG = 8,         /* scale not finite and > 0, workspace too small,
+                             drop probability out of range                 */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -203,6 +204,52 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                              int64_t N, int64_t d, fa_dtype dt, float scale,
                              int causal, const uint8_t* mask, int64_t block_m,
                              int64_t block_n, void* stream);
+
+/*
+ * fa_fwd_dropout — forward pass with dropout on the attention probabilities
+ * ([XYZ] key ideas: dropout is among the steps fused into the one attention
+ * kernel, with the matrix products, the mask and the softmax).
+ *
+ *   P = softmax(S) as in fa_fwd,  O = (Z * P / (1 - p)) V,
+ *   lse_i = ln sum_j exp(S_ij)   (of P itself: dropout does not change it),
+ * where Z_ij is 0 (dropped) or 1 (kept).  The pages define neither the
+ * dropout nor its random numbers; this library fixes them as follows.
+ *   p      : p_drop quantised to t / 256 with t = round(256 p_drop); t must
+ *            be <= 255 (0 <= p_drop <= 255/256, else FA_ERR_ARG).  t = 0
+ *            gives exactly fa_fwd.
+ *   Z_ij   : kept iff u >= t, u the random byte of element (bh, i, j),
+ *            bh = b*H + h: byte (j & 3) (bits 8(j&3) .. 8(j&3)+7) of word
+ *            (i & 3) of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ *            Random Numbers: As Easy as 1, 2, 3", SC 2011) applied to the
+ *            counter (i >> 2, j >> 2, bh, 0) with the key (seed & 0xffffffff,
+ *            seed >> 32).  The mask depends only on (seed, bh, i, j), not on
+ *            the launch configuration; call fa_bwd_dropout with the same
+ *            seed and p_drop.
+ * Other arguments, outputs and errors as fa_fwd.  FA_BF16 only (FA_F32
+ * returns FA_ERR_UNSUPPORTED); no block mask.
+ */
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t N,
+                         int64_t d, fa_dtype dt, float scale, int causal,
+                         float p_drop, uint64_t seed, void* stream);
+
+/*
+ * fa_bwd_dropout — backward pass of fa_fwd_dropout (same q, k, v, scale,
+ * causal, p_drop, seed; o and lse from that call): the exact gradient of
+ * L = sum(O * dO) with the mask Z fixed,
+ *   dV = (Z * P / (1 - p))^T dO,   dP = Z * (dO V^T) / (1 - p),
+ *   D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij),   dS = P * (dP - D),
+ *   dQ = scale dS K,   dK = scale dS^T Q,
+ * by recomputation as fa_bwd (the mask is regenerated, never stored).
+ * Arguments, workspace, outputs and errors as fa_bwd and fa_fwd_dropout.
+ */
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t N, int64_t d, fa_dtype dt, float scale,
+                         int causal, float p_drop, uint64_t seed,
+                         void* stream);
 
 /* Bytes of workspace fa_bwd and fa_bwd_blocksparse need (0 for empty
  * problems). */

@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
 )
 from .dropout import (  # noqa: F401,E402
     attention_bwd_dropout_head,
+    attention_dq_dropout_rows,
     attention_fwd_dropout_head,
     dropout_bytes,
     dropout_keep,

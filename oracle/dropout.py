@@ -46,6 +46,7 @@ __all__ = [
     "dropout_keep",
     "attention_fwd_dropout_head",
     "attention_bwd_dropout_head",
+    "attention_dq_dropout_rows",
 ]
 
 # Philox4x32 constants (Salmon et al. 2011, section 5: the two multipliers
@@ -115,18 +116,19 @@ def dropout_keep(bh, n_q, n_k, seed, t):
     return dropout_bytes(bh, np.arange(n_q), np.arange(n_k), seed) >= t
 
 
-def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh):
+def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None):
     """O and LSE of one head with dropout on P (module docstring):
       S = scale Q K^T (masked entries -inf),  P = softmax(S),
       O = (Z * P * 256 / (256 - t)) V,  LSE_i = ln(sum_j exp(S_ij)).
-    Returns O (n_q, dv) and LSE (n_q,), float64."""
+    Returns O (n_q, dv) and LSE (n_q,), float64; with ``rows`` only those
+    query rows (each row of O depends on its own row of S alone)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     n_q, n_k = q.shape[0], k.shape[0]
-    r = np.arange(n_q)
-    S = scale * (q @ k.T)
+    r = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    S = scale * (q[r] @ k.T)
     S = np.where(visible(r, n_k, causal), S, NEG_INF)
     P, m, l = _softmax_rows(S)
-    Z = dropout_keep(bh, n_q, n_k, seed, t)
+    Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
     Pd = np.where(Z, P, 0.0) * (256.0 / (256.0 - t))
     O = Pd @ v
     with np.errstate(divide="ignore"):
@@ -154,3 +156,22 @@ def attention_bwd_dropout_head(q, k, v, do, scale, causal, t, seed, bh):
     dq = scale * (dS @ k)
     dk = scale * (dS.T @ q)
     return dq, dk, dv
+
+
+def attention_dq_dropout_rows(q, k, v, do, scale, causal, t, seed, bh, rows):
+    """dQ of the given query rows of one head with dropout on P: row i of dQ
+    needs only row i of P, dP and D (same chain rule as
+    ``attention_bwd_dropout_head``), so heads too long to materialise can be
+    checked row by row."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n_k = k.shape[0]
+    r = np.asarray(rows, dtype=np.int64)
+    S = scale * (q[r] @ k.T)
+    S = np.where(visible(r, n_k, causal), S, NEG_INF)
+    P, _, _ = _softmax_rows(S)
+    Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
+    c = 256.0 / (256.0 - t)
+    dP = np.where(Z, do[r] @ v.T, 0.0) * c
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    return scale * (dS @ k)

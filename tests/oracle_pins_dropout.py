@@ -201,6 +201,43 @@ def check_brute_force_python(drp):
             assert abs(O[i, c] - want) <= 1e-12, f"O[{i},{c}]"
 
 
+def check_row_subsets(drp):
+    """The row-restricted forward and dQ equal the full-head results on those
+    rows (the full-head functions are pinned above)."""
+    r = np.random.default_rng(35)
+    for n, d, causal, t in ((40, 8, True, 51), (33, 4, False, 200)):
+        q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+        rows = np.array([0, 3, 4, 17, n - 1])
+        O, L = drp.attention_fwd_dropout_head(q, k, v, 0.6, causal, t, 9, 3)
+        Or, Lr = drp.attention_fwd_dropout_head(q, k, v, 0.6, causal, t, 9, 3,
+                                                rows=rows)
+        _close(Or, O[rows], 1e-13, "forward rows")
+        _close(Lr, L[rows], 1e-13, "LSE rows")
+        dq = drp.attention_bwd_dropout_head(q, k, v, do, 0.6, causal, t, 9,
+                                            3)[0]
+        dqr = drp.attention_dq_dropout_rows(q, k, v, do, 0.6, causal, t, 9, 3,
+                                            rows)
+        _close(dqr, dq[rows], 1e-12, "dQ rows")
+
+
+def check_d_identity(drp):
+    """sum_j P_ij dP_ij = sum_c dO_ic O_ic: the row statistic the backward
+    needs can be formed from the dropout forward's output (P from the
+    dropout-free oracle, Z from the mask function, dP from its definition)."""
+    r = np.random.default_rng(36)
+    n, d, t, seed, bh = 23, 6, 77, 31337, 2
+    for causal in (False, True):
+        q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+        S = 0.5 * (q @ k.T)
+        S = np.where(plain.visible(np.arange(n), n, causal), S, -np.inf)
+        S = S - S.max(axis=1, keepdims=True)
+        P = np.exp(S) / np.exp(S).sum(axis=1, keepdims=True)
+        Z = drp.dropout_keep(bh, n, n, seed, t)
+        dP = np.where(Z, do @ v.T, 0.0) * 256.0 / (256.0 - t)
+        O, _ = drp.attention_fwd_dropout_head(q, k, v, 0.5, causal, t, seed, bh)
+        _close((P * dP).sum(axis=1), (do * O).sum(axis=1), 1e-12, "D identity")
+
+
 ALL_CHECKS = [
     check_philox_kat,
     check_mask_layout,
@@ -210,4 +247,6 @@ ALL_CHECKS = [
     check_unbiased,
     check_finite_differences,
     check_brute_force_python,
+    check_row_subsets,
+    check_d_identity,
 ]

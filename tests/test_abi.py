@@ -264,3 +264,35 @@ def test_row_count_limits(lib):
     assert bwd(lib, B=1 << 20, H=1 << 10, N=32, d=64, ws_bytes=0) == FA_ERR_SHAPE
     assert splitkv(lib, B=1 << 25, H=1 << 5, Nq=32, Nk=32, ws_bytes=0) == FA_ERR_SHAPE
     assert lib.fa_fwd_splitkv_chunks(1 << 25, 1 << 5, 32, 32, 128, 0) == 0
+
+
+def fwd_drop(lib, p=0.1, seed=1, dt=BF16, N=128, d=64, q=P, scale=0.125):
+    return lib.fa_fwd_dropout(q, P, P, P, P, 1, 1, N, d, dt, scale, 0, p,
+                              seed, None)
+
+
+def bwd_drop(lib, p=0.1, seed=1, dt=BF16, N=128, d=64, ws_bytes=1 << 20,
+             ws=P):
+    return lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, ws, ws_bytes, 1, 1,
+                              N, d, dt, 0.125, 1, p, seed, None)
+
+
+def test_dropout_validation(lib):
+    # drop probability: round(256 p) must lie in [0, 255]
+    for bad in (-0.01, 255.6 / 256, 1.0, 2.0, float("nan"), float("inf")):
+        assert fwd_drop(lib, p=bad) == FA_ERR_ARG, bad
+        assert bwd_drop(lib, p=bad) == FA_ERR_ARG, bad
+    # bf16 only
+    assert fwd_drop(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    assert bwd_drop(lib, dt=F32) == FA_ERR_UNSUPPORTED
+    # shared checks come first and keep their codes
+    assert fwd_drop(lib, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd_drop(lib, N=-1) == FA_ERR_SHAPE
+    assert fwd_drop(lib, scale=0.0) == FA_ERR_ARG
+    assert fwd_drop(lib, q=None) == FA_ERR_NULL
+    assert fwd_drop(lib, q=MISALIGNED) == FA_ERR_ALIGN
+    assert bwd_drop(lib, ws=None) == FA_ERR_NULL
+    assert bwd_drop(lib, ws_bytes=16) == FA_ERR_ARG
+    # empty problems do nothing, whatever the seed
+    assert fwd_drop(lib, N=0, seed=2**64 - 1) == FA_OK
+    assert bwd_drop(lib, N=0, seed=0) == FA_OK

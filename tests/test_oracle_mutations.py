@@ -139,6 +139,12 @@ DROPOUT_MUTATIONS = [
     ("bwd: dV from the undropped P", "dv = Pd.T @ do", "dv = P.T @ do", 0),
     ("bwd: D from the dropped P", "D = (P * dP).sum(axis=1)",
      "D = (Pd * dP).sum(axis=1)", 0),
+    ("dq rows: dP not rescaled", "dP = np.where(Z, do[r] @ v.T, 0.0) * c",
+     "dP = np.where(Z, do[r] @ v.T, 0.0)", 0),
+    ("dq rows: D term dropped", "dS = P * (dP - D[:, None])\n    return",
+     "dS = P * dP\n    return", 0),
+    ("fwd rows: mask of the first rows", "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t",
+     "Z = dropout_bytes(bh, np.arange(len(r)), np.arange(n_k), seed) >= t", 0),
 ]
 
 
