@@ -443,6 +443,11 @@ def main():
             calib_copy(args.calib_copy_mb)
         decode_line(args)
         return
+    if _wl.workload(args.workload).get("p_drop"):
+        print(f"{args.workload} is a dropout workload: bench.py --all times it "
+              "(fa_fwd_dropout, fa_bwd_dropout); the per-kernel step here "
+              "times the dropout-free passes.", file=sys.stderr)
+        sys.exit(2)
     r = time_workload(args.workload, args.steps, args.warmup,
                       args.calib_copy_mb)
     B, H, N, d = r["B"], r["H"], r["N"], r["d"]
