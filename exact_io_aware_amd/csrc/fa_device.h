@@ -195,7 +195,10 @@ __device__ __forceinline__ int xcd_logical_id(int g, int total) {
 // XCD's L2 when its tiles fill the XCD; when a head has fewer tiles than an
 // XCD has workgroup slots, bundle = slots / tiles (rounded up) keeps the
 // longest-first order across the XCD.  Returns the head and the tile's rank
-// (0 = heaviest).
+// (0 = heaviest).  Used where a workgroup takes one tile (4-wave forward and
+// dQ instances, block-sparse instances); the dense one-workgroup-per-CU
+// kernels instead pair tiles u and n-1-u so that all workgroups carry equal
+// work.
 struct CausalPlace {
   int head, rank;
 };
