@@ -18,11 +18,13 @@
 //
 // Three kernels, no atomics:
 //   preprocess : D_i and lse_i * log2(e) per row (a streaming pass).
-//   dkdv       : a workgroup owns 128 keys (32 per wave, K and V held in
-//                registers) and sweeps the query tiles, accumulating dK^T
-//                and dV^T in registers; each is written once.
-//   dq         : a workgroup owns 128 queries (32 per wave, Q and dO held in
-//                registers) and sweeps the key tiles, accumulating dQ^T.
+//   dkdv       : a workgroup owns 128 keys (32 per wave and query half; K
+//                and V held in LDS for the workgroup's life) and sweeps the
+//                query tiles, accumulating dK^T and dV^T in registers; each
+//                is written once.
+//   dq         : a workgroup owns 128 or 256 queries (32 per wave, Q and dO
+//                held in registers) and sweeps the key tiles, accumulating
+//                dQ^T.
 // All contractions run on v_mfma_f32_32x32x16_bf16.  The dkdv pass computes
 // S = Q K^T so that each lane owns one key (the N index of the D layout); P
 // and dS then already have the B-operand layout for the contractions over
