@@ -391,3 +391,14 @@ def fa_bwd_dq(q, k, v, do, workspace, dq, scale=None, causal=False):
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
             ws_bytes, B, H, N, d, _dtype_code(q), _scale(scale, d),
             int(bool(causal)), _stream(q.device)))
+
+
+# Short names for the common calls (the same functions).
+fwd = fa_fwd
+bwd = fa_bwd
+
+
+def fwd_blocksparse(q, k, v, mask, block=128, scale=None, causal=False):
+    """fa_fwd_blocksparse with square mask blocks of ``block`` rows/keys."""
+    return fa_fwd_blocksparse(q, k, v, mask, block, block, scale=scale,
+                              causal=causal)

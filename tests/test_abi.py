@@ -296,3 +296,9 @@ def test_dropout_validation(lib):
     # empty problems do nothing, whatever the seed
     assert fwd_drop(lib, N=0, seed=2**64 - 1) == FA_OK
     assert bwd_drop(lib, N=0, seed=0) == FA_OK
+
+
+def test_binding_short_names():
+    from exact_io_aware_amd import fa
+    assert fa.fwd is fa.fa_fwd and fa.bwd is fa.fa_bwd
+    assert callable(fa.fwd_blocksparse)
