@@ -226,7 +226,8 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
  *            the launch configuration; call fa_bwd_dropout with the same
  *            seed and p_drop.
  * Other arguments, outputs and errors as fa_fwd.  FA_BF16 only (FA_F32
- * returns FA_ERR_UNSUPPORTED); no block mask.
+ * returns FA_ERR_UNSUPPORTED); no block mask.  (The shape limits shared by
+ * every call keep B*H below 2^31, so bh always fits its counter word.)
  */
 fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
                          float* lse, int64_t B, int64_t H, int64_t N,
