@@ -461,7 +461,8 @@ __device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br,
 // query rows share each K/V tile, halving the tile traffic into LDS per row.
 // Otherwise a workgroup has 4 waves and two run per CU; the block-sparse
 // kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
-// row of the mask.
+// row of the mask.  DROP instances apply dropout to P (Dropout, with the
+// keep bits drawn per 4 x 4 score block from the seed, head, row and key).
 template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
