@@ -1,6 +1,7 @@
 """The hot path under HIP-graph capture: the library enqueues only kernel
 launches (no memsets, no allocations of its own), so a forward + backward
-step, and the split-KV decode, can be captured once and replayed.  Every
+step (with or without dropout), and the split-KV decode, can be captured once
+and replayed.  Every
 replay is compared bitwise with the eager result, with the program's own
 eager work and synchronisations between replays."""
 
@@ -78,3 +79,33 @@ def test_graph_splitkv_decode(dev):
                           out=o_g, lse=lse_g)
     noise = torch.ones(1024, device=dev)
     _replay_and_check(g, [o_g, lse_g], ref, noise)
+
+
+def test_graph_dropout_step(dev):
+    # The dropout mask is a function of (seed, head, row, key) alone, so
+    # replays reproduce the eager step bit for bit.
+    B, H, N, d, p, seed = 1, 4, 320, 128, 0.2, 123456789
+    x = gen(B, H, N, d, seed=83, with_do=True, dev=dev)
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o, lse = fa.fa_fwd_dropout(q, k, v, p, seed, causal=True)
+    ref = [o.clone(), lse.clone(),
+           *fa.fa_bwd_dropout(q, k, v, o, do, lse, p, seed, causal=True)]
+    torch.cuda.synchronize()
+    o_g, lse_g = torch.empty_like(o), torch.empty_like(lse)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=dev)
+             for _ in range(3)]
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):         # warm-up on the capture stream
+        fa.fa_fwd_dropout(q, k, v, p, seed, causal=True, out=o_g, lse=lse_g)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_fwd_dropout(q, k, v, p, seed, causal=True, out=o_g, lse=lse_g)
+        fa.fa_bwd_dropout(q, k, v, o_g, do, lse_g, p, seed, causal=True,
+                          workspace=ws, dq=grads[0], dk=grads[1], dv=grads[2])
+    noise = torch.ones(1024, device=dev)
+    _replay_and_check(g, [o_g, lse_g, *grads], ref, noise)
