@@ -18,8 +18,7 @@ Pages cited (titles as published):
            (llm-systems-engineering.pages.dev)
   [Q67]    "FlashAttention：在线 softmax 与 IO-aware 注意力" (quant67.com)
 
-Readings of points the pages leave open (each is also listed in the design
-notes of the repository):
+Readings of points the pages leave open:
   * The saved per-row statistic is one natural-log logsumexp of the *scaled*
     scores, LSE_i = m_i + ln(l_i); the pages save the pair (m, l)
     ([TLDR] backward section, [XYZ] key ideas, [Q67] section 5).

@@ -8,7 +8,7 @@ helpers with the HIP library and imports nothing from it.
 [XYZ] (key ideas, kernel fusion) lists dropout among the steps fused into the
 one attention kernel, next to the matrix products, the mask and the softmax.
 The pages define neither the dropout nor its random numbers.  Readings taken
-here (each is also listed in the design notes of the repository):
+here:
 
   * Dropout acts on the probability matrix: P~ = Z * P / (1 - p) with
     Z_ij in {0, 1} drawn independently, P(Z_ij = 0) = p, and O = P~ V.  The
