@@ -12,7 +12,6 @@ from .attention import (  # noqa: F401
     attention_fwd,
     attention_fwd_head,
     causal_tiles_visited,
-    expand_block_mask,
     tiled_fwd_fa1_head,
     tiled_fwd_head,
     visible,

@@ -49,7 +49,6 @@ __all__ = [
     "tiled_fwd_head",
     "tiled_fwd_fa1_head",
     "causal_tiles_visited",
-    "expand_block_mask",
     "attention_decode_head",
 ]
 
@@ -85,11 +84,6 @@ def visible(rows, n_keys, causal=False, block_mask=None, block_m=128,
         bm = np.asarray(block_mask) != 0
         vis &= bm[rows[:, None] // block_m, cols[None, :] // block_n]
     return vis
-
-
-def expand_block_mask(block_mask, n, block_m, block_n):
-    """Element-level N x N boolean mask from a block mask (no causal rule)."""
-    return visible(np.arange(n), n, False, block_mask, block_m, block_n)
 
 
 # ---------------------------------------------------------------------------
@@ -164,21 +158,45 @@ def attention_decode_head(q, k, v, scale, causal=False):
     return O, LSE
 
 
+def _each_head(fn, heads, workers):
+    """fn(idx) for every head index, in order.  Heads are independent, so
+    with workers > 1 they run on a thread pool (NumPy's matrix products and
+    ufuncs release the interpreter lock), each with a single BLAS thread."""
+    heads = list(heads)
+    if workers <= 1 or len(heads) <= 1:
+        return [fn(idx) for idx in heads]
+    import concurrent.futures
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1, user_api="blas")
+    except ImportError:  # pragma: no cover - threadpoolctl is optional
+        limit = contextlib.nullcontext()
+    with limit, concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, heads))
+
+
 def attention_fwd(Q, K, V, scale, causal=False, block_mask=None, block_m=128,
-                  block_n=128, heads=None, row_chunk=1024):
-    """Batched forward over leading dims: Q, K, V of shape (..., N, d).
+                  block_n=128, heads=None, row_chunk=1024, workers=1):
+    """Batched forward over leading dims: Q, K, V of shape (..., N, d); each
+    head is ``attention_fwd_head`` of that head's slices.
 
     ``heads`` optionally restricts the work to a list of leading-index tuples
-    (the other heads of the returned arrays stay NaN).
+    (the other heads of the returned arrays stay NaN); ``workers`` > 1 runs
+    the heads on that many threads.
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     lead = Q.shape[:-2]
     O = np.full(lead + (Q.shape[-2], V.shape[-1]), np.nan)
     LSE = np.full(lead + (Q.shape[-2],), np.nan)
-    for idx in (np.ndindex(*lead) if heads is None else heads):
-        O[idx], LSE[idx] = attention_fwd_head(
-            Q[idx], K[idx], V[idx], scale, causal, block_mask, block_m,
-            block_n, row_chunk=row_chunk)
+    idxs = list(np.ndindex(*lead) if heads is None else heads)
+
+    def one(idx):
+        return attention_fwd_head(Q[idx], K[idx], V[idx], scale, causal,
+                                  block_mask, block_m, block_n,
+                                  row_chunk=row_chunk)
+    for idx, (o, lse) in zip(idxs, _each_head(one, idxs, workers)):
+        O[idx], LSE[idx] = o, lse
     return O, LSE
 
 
@@ -249,17 +267,24 @@ def attention_bwd_rows(q, k, v, do, scale, rows, causal=False,
 
 
 def attention_bwd(Q, K, V, dO, scale, causal=False, block_mask=None,
-                  block_m=128, block_n=128, heads=None, row_chunk=1024):
-    """Batched backward over leading dims (see ``attention_bwd_head``)."""
+                  block_m=128, block_n=128, heads=None, row_chunk=1024,
+                  workers=1):
+    """Batched backward over leading dims: each head is
+    ``attention_bwd_head`` of that head's slices (``heads`` and ``workers``
+    as in ``attention_fwd``)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     lead = Q.shape[:-2]
     dQ = np.full(Q.shape, np.nan)
     dK = np.full(K.shape, np.nan)
     dV = np.full(V.shape, np.nan)
-    for idx in (np.ndindex(*lead) if heads is None else heads):
-        dQ[idx], dK[idx], dV[idx] = attention_bwd_head(
-            Q[idx], K[idx], V[idx], dO[idx], scale, causal, block_mask,
-            block_m, block_n, row_chunk=row_chunk)
+    idxs = list(np.ndindex(*lead) if heads is None else heads)
+
+    def one(idx):
+        return attention_bwd_head(Q[idx], K[idx], V[idx], dO[idx], scale,
+                                  causal, block_mask, block_m, block_n,
+                                  row_chunk=row_chunk)
+    for idx, (dq, dk, dv) in zip(idxs, _each_head(one, idxs, workers)):
+        dQ[idx], dK[idx], dV[idx] = dq, dk, dv
     return dQ, dK, dV
 
 

@@ -509,6 +509,68 @@ def check_bwd_rows(orc):
                 _close(dv_t[8:], Tdv[8:], 1e-12, "causal tail keys dV")
 
 
+def check_batched_wrappers(orc):
+    """The batched forms ``attention_fwd`` and ``attention_bwd`` (every
+    workload parity test and the smoke test go through them) against
+    PyTorch's float64 attention and autograd, head by head: distinct data in
+    every (b, h), non-square blocks (block_m = 4, block_n = 2, so a swap of
+    the two changes the visible set), a block row with no visible key, causal
+    and not, a ragged N; the element mask is expanded here with Python
+    loops.  Also: ``heads`` restricts the work and leaves the other heads
+    NaN, and ``workers`` > 1 gives the same values."""
+    r = _rng(42)
+    B, H, n, d, dv = 2, 3, 11, 4, 3
+    bm_, bn_ = 4, 2
+    Q, K = r.standard_normal((B, H, n, d)), r.standard_normal((B, H, n, d))
+    V, dO = r.standard_normal((B, H, n, dv)), r.standard_normal((B, H, n, dv))
+    mask = (r.random((3, 6)) < 0.6).astype(np.uint8)
+    mask[1] = 0                                  # rows 4..7 see no key
+    mask[0, 0] = mask[2, 5] = 1
+    assert not np.array_equal(mask, mask.T[:3, :3])
+    scale = 0.55
+    for causal in (False, True):
+        for m in (None, mask):
+            O, lse = orc.attention_fwd(Q, K, V, scale, causal, m, bm_, bn_)
+            dq, dk, dv_ = orc.attention_bwd(Q, K, V, dO, scale, causal, m,
+                                            bm_, bn_)
+            for b in range(B):
+                for h in range(H):
+                    vis = np.array([[(j <= i or not causal) and
+                                     (m is None or m[i // bm_][j // bn_] != 0)
+                                     for j in range(n)] for i in range(n)])
+                    live = vis.any(axis=1)
+                    e2 = vis.copy()
+                    e2[~live] = True
+                    To, Tl, Tdq, Tdk, Tdv = _torch_reference(
+                        Q[b, h], K[b, h], V[b, h],
+                        np.where(live[:, None], dO[b, h], 0.0), scale, False,
+                        e2)
+                    tag = f"batched ({b},{h}) causal={causal} mask={m is not None}"
+                    _close(O[b, h][live], To[live], 1e-12, tag + " O")
+                    _close(lse[b, h][live], Tl[live], 1e-12, tag + " LSE")
+                    assert np.all(O[b, h][~live] == 0.0), tag + " empty O"
+                    assert np.all(np.isneginf(lse[b, h][~live])), tag
+                    _close(dq[b, h][live], Tdq[live], 1e-12, tag + " dQ")
+                    assert np.all(dq[b, h][~live] == 0.0), tag + " empty dQ"
+                    _close(dk[b, h], Tdk, 1e-12, tag + " dK")
+                    _close(dv_[b, h], Tdv, 1e-12, tag + " dV")
+    O_all, l_all = orc.attention_fwd(Q, K, V, scale, True, mask, bm_, bn_)
+    O_one, l_one = orc.attention_fwd(Q, K, V, scale, True, mask, bm_, bn_,
+                                     heads=[(1, 2)])
+    assert np.array_equal(O_one[1, 2], O_all[1, 2])
+    assert np.isnan(O_one[0]).all() and np.isnan(l_one[1, :2]).all()
+    O_t, l_t = orc.attention_fwd(Q, K, V, scale, True, mask, bm_, bn_,
+                                 workers=4)
+    _close(O_t, O_all, 1e-13, "threaded O")
+    _close(np.nan_to_num(l_t, neginf=-1e300),
+           np.nan_to_num(l_all, neginf=-1e300), 1e-13, "threaded LSE")
+    g_all = orc.attention_bwd(Q, K, V, dO, scale, True, mask, bm_, bn_)
+    g_t = orc.attention_bwd(Q, K, V, dO, scale, True, mask, bm_, bn_,
+                            workers=4)
+    for a, t in zip(g_all, g_t):
+        _close(t, a, 1e-13, "threaded gradients")
+
+
 ALL_CHECKS = [
     check_fig1_divide_last,
     check_fig2_streamed_pairs,
@@ -527,4 +589,5 @@ ALL_CHECKS = [
     check_block_sparse,
     check_decode,
     check_bwd_rows,
+    check_batched_wrappers,
 ]

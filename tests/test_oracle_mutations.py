@@ -76,6 +76,28 @@ MUTATIONS = [
      "l_new = l + c_blk * l_blk", 0),
     ("FA1: output not un-normalised",
      "num = (l * c_old)[:, None] * o", "num = c_old[:, None] * o", 0),
+    ("batched fwd: block sizes swapped",
+     "block_mask, block_m, block_n,\n                                  row_chunk",
+     "block_mask, block_n, block_m,\n                                  row_chunk", 0),
+    ("batched fwd: causal rule dropped",
+     "scale, causal,\n                                  block_mask",
+     "scale, False,\n                                  block_mask", 0),
+    ("batched fwd: keys of the neighbouring head",
+     "attention_fwd_head(Q[idx], K[idx], V[idx]",
+     "attention_fwd_head(Q[idx], K[idx[:-1] + ((idx[-1] + 1) % K.shape[-3],)], V[idx]", 0),
+    ("batched fwd: LSE of another head",
+     "O[idx], LSE[idx] = o, lse", "O[idx], LSE[idx[::-1]] = o, lse", 0),
+    ("batched bwd: block sizes swapped",
+     "causal, block_mask, block_m, block_n,\n                                  row_chunk",
+     "causal, block_mask, block_n, block_m,\n                                  row_chunk", 0),
+    ("batched bwd: dO of the neighbouring head",
+     "V[idx], dO[idx], scale", "V[idx], dO[idx[:-1] + ((idx[-1] + 1) % dO.shape[-3],)], scale", 0),
+    ("batched bwd: dK and dV slots swapped",
+     "dQ[idx], dK[idx], dV[idx] = dq, dk, dv",
+     "dQ[idx], dK[idx], dV[idx] = dq, dv, dk", 0),
+    ("batched bwd: causal rule dropped",
+     "dO[idx], scale,\n                                  causal,",
+     "dO[idx], scale,\n                                  False,", 0),
 ]
 
 
