@@ -398,6 +398,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 
   // Add the two query halves' partial sums through LDS, then store once.
+  // The reduction buffer reuses the tile space: every fill issued by this
+  // wave (K and V at the top, even when no query tile is visited) must have
+  // landed before any wave writes there.
+  wait_dma();
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
   auto slot = [&](int t, int db, int i) {
