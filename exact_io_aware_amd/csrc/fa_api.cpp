@@ -68,7 +68,9 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
                      float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
                      fa_dtype dt, float scale, int causal, const uint8_t* mask,
                      int64_t block_m, int64_t block_n, bool sparse_call,
-                     void* stream, int drop_t = 0, uint64_t seed = 0) {
+                     void* stream, int drop_t = 0, uint64_t seed = 0,
+                     bool count_call = false, int32_t* visits = nullptr,
+                     size_t visits_len = 0) {
   bool empty = false;
   int64_t bh = 0;
   fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
@@ -80,11 +82,19 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
       return FA_ERR_MASK;
     }
   }
+  if (count_call && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       !aligned(o, 16) || !aligned(lse, 4)) {
     return FA_ERR_ALIGN;
+  }
+  if (count_call) {
+    if (!visits) return FA_ERR_NULL;
+    if (!aligned(visits, 4)) return FA_ERR_ALIGN;
+    int rows = 0, cols = 0;
+    fa::fwd_bf16_tile_grid((int)d, mask != nullptr, &rows, &cols);
+    if (visits_len < (size_t)(bh * ((N + rows - 1) / rows))) return FA_ERR_ARG;
   }
   fa::FwdArgs a{};
   a.q = q;
@@ -104,6 +114,7 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
   a.drop_t = drop_t;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
+  a.visits = count_call ? visits : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return from_hip(dt == FA_BF16 ? fa::launch_fwd_bf16(a, s)
                                 : fa::launch_fwd_f32(a, s));
@@ -434,6 +445,68 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                             true, causal, &a, &empty, mask, block_m, block_n,
                             true);
   if (st != FA_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(run_pre(a, dt, s));
+  if (st != FA_OK) return st;
+  st = from_hip(run_dkdv(a, dt, s));
+  if (st != FA_OK) return st;
+  return from_hip(run_dq(a, dt, s));
+}
+
+fa_status fa_tile_grid(int pass, int64_t d, int sparse, int64_t* rows,
+                       int64_t* cols) {
+  if (!rows || !cols) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  int r = 0, c = 0;
+  switch (pass) {
+    case 0: fa::fwd_bf16_tile_grid((int)d, sparse != 0, &r, &c); break;
+    case 1: fa::bwd_dkdv_tile_grid((int)d, &r, &c); break;
+    case 2: fa::bwd_dq_tile_grid((int)d, sparse != 0, &r, &c); break;
+    default: return FA_ERR_ARG;
+  }
+  *rows = r;
+  *cols = c;
+  return FA_OK;
+}
+
+fa_status fa_fwd_tile_visits(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, int32_t* visits,
+                             size_t visits_len, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, dt, scale, causal, mask,
+                    block_m, block_n, true, stream, 0, 0, true, visits,
+                    visits_len);
+}
+
+fa_status fa_bwd_tile_visits(const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, int32_t* visits_kv,
+                             size_t kv_len, int32_t* visits_q, size_t q_len,
+                             void* stream) {
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            workspace, workspace_bytes, B, H, N, d, dt, scale,
+                            true, causal, &a, &empty, mask, block_m, block_n,
+                            true);
+  if (st != FA_OK) return st;
+  if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  if (!visits_kv || !visits_q) return FA_ERR_NULL;
+  if (!aligned(visits_kv, 4) || !aligned(visits_q, 4)) return FA_ERR_ALIGN;
+  int rows = 0, cols = 0;
+  fa::bwd_dkdv_tile_grid((int)d, &rows, &cols);
+  if (kv_len < (size_t)(a.bh * ((N + cols - 1) / cols))) return FA_ERR_ARG;
+  fa::bwd_dq_tile_grid((int)d, mask != nullptr, &rows, &cols);
+  if (q_len < (size_t)(a.bh * ((N + rows - 1) / rows))) return FA_ERR_ARG;
+  a.visits_kv = visits_kv;
+  a.visits_q = visits_q;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = from_hip(run_pre(a, dt, s));
   if (st != FA_OK) return st;

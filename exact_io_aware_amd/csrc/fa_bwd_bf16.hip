@@ -147,7 +147,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ dV, int n, int n_ktiles, int total,
                      int bundle, float c_log2, float scale,
                      const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n, Dropout drop) {
+                     int mask_cols, int block_m, int block_n, Dropout drop,
+                     int* __restrict__ visits) {
   using T = KVTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
 
@@ -274,10 +275,12 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // are skipped.  PAR is the stage parity when known at compile time (every
   // LDS address is then a register plus an immediate), else -1 (then
   // `stage`).  `qt_next` is the tile that follows.
+  int nvis = 0;  // query tiles visited (diagnostic count)
   auto tile = [&](auto mask_tag, auto par_tag, int qt, int stage_rt, int qt_next) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     const int stage = (PAR >= 0) ? PAR : stage_rt;
+    ++nvis;
     wait_dma();
     __syncthreads();
     if (qt_next < n_qt) issue_stage(qt_next, stage ^ 1);
@@ -439,6 +442,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
     }
   }
+  if (visits != nullptr && w == 0 && lane == 0) {
+    visits[(int64_t)head * n_ktiles + kt] = nvis;
+  }
   };
 
   run_tile(kt_a);
@@ -482,7 +488,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    int n, int n_qtiles, int total, int bundle, float c_log2,
                    float scale,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
-                   int block_n, Dropout drop) {
+                   int block_n, Dropout drop, int* __restrict__ visits) {
   using T = QTile<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
 
@@ -597,10 +603,12 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     return __builtin_amdgcn_readfirstlane(kt);
   };
+  int nvis = 0;  // key tiles visited (diagnostic count)
   auto tile = [&](auto mask_tag, auto par_tag, int kt, int stage_rt, int kt_next) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int PAR = decltype(par_tag)::value;
     const int stage = (PAR >= 0) ? PAR : stage_rt;
+    ++nvis;
     wait_dma();
     __syncthreads();
     if (kt_next < kt_end) fill(kt_next, stage ^ 1);
@@ -699,6 +707,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
     }
   }
+  if (visits != nullptr && w == 0 && lane == 0) {
+    visits[(int64_t)head * n_qtiles + qt] = nvis;
+  }
   };
 
   run_tile(qt_a);
@@ -731,7 +742,7 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
                        (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
                        causal_bundle(n_kt, 1), a.scale * kLog2e, a.scale,
                        a.mask, a.mask_cols, a.block_m, a.block_n,
-                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi), a.visits_kv);
 }
 
 // d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
@@ -750,7 +761,7 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
                        (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
                        causal_bundle(n_qt, NW == 8 ? 1 : 2), a.scale * kLog2e,
                        a.scale, a.mask, a.mask_cols, a.block_m, a.block_n,
-                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi), a.visits_q);
 }
 
 // Block-sparse, dropout (dense only) or neither.
@@ -776,6 +787,16 @@ hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+void bwd_dkdv_tile_grid(int d, int* rows, int* cols) {
+  *rows = (d == 128) ? KVTile<128>::BRQ : KVTile<64>::BRQ;
+  *cols = (d == 128) ? KVTile<128>::BCK : KVTile<64>::BCK;
+}
+
+void bwd_dq_tile_grid(int d, bool sparse, int* rows, int* cols) {
+  *rows = (d == 128 && !sparse) ? QTile<128, 8>::BRQ : QTile<64, 4>::BRQ;
+  *cols = (d == 128) ? QTile<128, 8>::BCK : QTile<64, 4>::BCK;
+}
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s) {
   return a.d == 128 ? pre_t<128>(a, s) : pre_t<64>(a, s);

@@ -348,8 +348,9 @@ struct FwdWave {
 
 // The key loop of one workgroup: key tiles first, next_on(first), ... up to
 // kt_end (exclusive), K and V of the keys filled into kbuf / vbuf (two
-// buffers each), each wave's online-softmax state in wv.  Every wave runs
-// the same pipeline step per key tile:
+// buffers each), each wave's online-softmax state in wv; `visited` receives
+// the number of key tiles visited.  Every wave runs the same pipeline step
+// per key tile:
 //   block A: the scores of tile `nxt` on the matrix cores while the vector
 //            units form tile `cur`'s probabilities;
 //   block B: tile `cur`'s PV product on the matrix cores while the vector
@@ -360,8 +361,9 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
                                          unsigned char* kbuf, unsigned char* vbuf,
                                          const bf16* Kh, const bf16* Vh,
                                          int n_keys, int first, int kt_end,
-                                         NextOn next_on) {
+                                         NextOn next_on, int& visited) {
   int cur = first;
+  visited = 0;
   if (cur < kt_end) {
     int nxt = next_on(cur);
     fill.k(Kh, cur * T::BC, n_keys, kbuf);
@@ -439,6 +441,7 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
       copy_b_to_a();
     }
     step(no{}, no{}, par_rt{}, it, sa, sb);
+    visited = it + 1;  // one step per visited key tile
   }
 }
 
@@ -463,13 +466,14 @@ __device__ __forceinline__ FwdPlace fwd_place(int n_qtiles, int total, int br,
 // kernel keeps 128 rows so that a workgroup's rows lie in one 128-row block
 // row of the mask.  DROP instances apply dropout to P (Dropout, with the
 // keep bits drawn per 4 x 4 score block from the seed, head, row and key).
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP, bool COUNT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int n, int n_qtiles, int total,
                      int bundle, float c_log2, const uint8_t* __restrict__ mask,
-                     int mask_cols, int block_m, int block_n, Dropout drop) {
+                     int mask_cols, int block_m, int block_n, Dropout drop,
+                     int* __restrict__ visits) {
   // (With dropout at d = 64 the key tile is 64 wide, as at d = 128: the
   // random bytes need registers that 128-key score tiles leave no room for.)
   using T = FwdTile<D, NW, (D == 128 || DROP) ? 64 : 128>;
@@ -530,8 +534,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
       return __builtin_amdgcn_readfirstlane(kt);
     };
-    key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on);
+    int nvis = 0;
+    key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on,
+             nvis);
     wv.store(O + hoff, LSE + (int64_t)pl.head * n);
+    // Diagnostic count of the key tiles this query tile visited (COUNT
+    // instances only).
+    if (COUNT && w == 0 && lane == 0) {
+      visits[(int64_t)pl.head * n_qtiles + q0 / T::BR] = nvis;
+    }
   };
 
   run_tile(pl.q0);
@@ -541,7 +552,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool COUNT = false>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = FwdTile<D, NW>;
@@ -550,15 +561,24 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int units = (CAUSAL && !SPARSE && NW == 8) ? (n_qtiles + 1) / 2 : n_qtiles;
   const int total = (int)(a.bh * units);
   const int bundle = causal_bundle(n_qtiles, NW == 8 ? 1 : 2);
-  return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, DROP>, dim3(total),
+  return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, DROP, COUNT>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
                        total, bundle, a.scale * kLog2e, a.mask, a.mask_cols,
-                       a.block_m, a.block_n, make_dropout(a.drop_t, a.seed_lo, a.seed_hi));
+                       a.block_m, a.block_n, make_dropout(a.drop_t, a.seed_lo, a.seed_hi),
+                       a.visits);
 }
 
 template <int D>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
+  if (a.visits) {  // diagnostic instances that also count visited tiles
+    if (a.mask) {
+      return a.causal ? launch_fwd<D, true, true, false, true>(a, s)
+                      : launch_fwd<D, false, true, false, true>(a, s);
+    }
+    return a.causal ? launch_fwd<D, true, false, false, true>(a, s)
+                    : launch_fwd<D, false, false, false, true>(a, s);
+  }
   if (a.mask) {  // (no dropout with a block mask)
     return a.causal ? launch_fwd<D, true, true, false>(a, s)
                     : launch_fwd<D, false, true, false>(a, s);
@@ -611,7 +631,8 @@ void splitkv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   int kt_end = min(kt0 + tiles_per_split, n_ktiles);
   if (CAUSAL) kt_end = min(kt_end, (q_off + min(qt * 32 + 32, nq) - 1) / T::BC + 1);
   auto next_on = [](int kt) -> int { return __builtin_amdgcn_readfirstlane(kt + 1); };
-  key_loop(wv, fill, kbuf, vbuf, Kh, Vh, nk, kt0, kt_end, next_on);
+  int nvis = 0;
+  key_loop(wv, fill, kbuf, vbuf, Kh, Vh, nk, kt0, kt_end, next_on, nvis);
 
   const int64_t prow = ((int64_t)split * bh + head) * nq;
   wv.store_partial(Opart + prow * D, LSEpart + prow);
@@ -674,6 +695,12 @@ hipError_t launch_splitkv_t(const SplitKvArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+void fwd_bf16_tile_grid(int d, bool sparse, int* rows, int* cols) {
+  const int nw = (d == 128 && !sparse) ? 8 : 4;
+  *rows = 32 * nw;
+  *cols = (d == 128) ? FwdTile<128, 8>::BC : FwdTile<64, 4>::BC;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   return a.d == 128 ? dispatch_mask<128>(a, s) : dispatch_mask<64>(a, s);

@@ -2,7 +2,8 @@
 // Not installed; the public interface is include/fa.h.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fa {
@@ -26,6 +27,7 @@ struct FwdArgs {
   int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
   uint32_t seed_lo = 0;    // dropout seed words
   uint32_t seed_hi = 0;
+  int* visits = nullptr;   // diagnostic: key tiles visited per query tile
 };
 
 struct BwdArgs {
@@ -52,6 +54,8 @@ struct BwdArgs {
   int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
   uint32_t seed_lo = 0;    // dropout seed words
   uint32_t seed_hi = 0;
+  int* visits_kv = nullptr;  // diagnostic: query tiles visited per key tile
+  int* visits_q = nullptr;   // diagnostic: key tiles visited per query tile
 };
 
 // Split-KV forward: nq queries (the last nq of the nk positions) against nk
@@ -86,5 +90,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdArgs& a, hipStream_t s);
+
+// Tile geometry of the bf16 kernels (rows x cols of one work tile and of
+// the tiles it visits): forward query tile x key tile, dK/dV query stage x
+// key tile, dQ query tile x key tile.
+void fwd_bf16_tile_grid(int d, bool sparse, int* rows, int* cols);
+void bwd_dkdv_tile_grid(int d, int* rows, int* cols);
+void bwd_dq_tile_grid(int d, bool sparse, int* rows, int* cols);
 
 }  // namespace fa

@@ -20,6 +20,7 @@ __all__ = [
     "fa_fwd_splitkv_chunks", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
     "fa_bwd_blocksparse", "fa_bwd_preprocess",
     "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
+    "fa_tile_grid", "fa_fwd_tile_visits", "fa_bwd_tile_visits",
     "fa_version", "library", "LIB_PATH",
 ]
 
@@ -47,7 +48,13 @@ def library():
         raise RuntimeError(
             f"HIP attention library not built ({LIB_PATH} missing); run "
             "__graft_entry__.build() first. There is no fallback path.")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(lib):
+    """Set the argument and result types of every entry point of a loaded
+    library (the signatures of include/fa.h); returns it."""
     P, I64, F, I, SZ, U64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64)
     sigs = {
@@ -68,6 +75,11 @@ def library():
                            P],
         "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
                            I64, I, F, I, F, U64, P],
+        "fa_tile_grid": [I, I64, I, P, P],
+        "fa_fwd_tile_visits": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
+                               I64, I64, P, SZ, P],
+        "fa_bwd_tile_visits": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
+                               I64, I, F, I, P, I64, I64, P, SZ, P, SZ, P],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -83,7 +95,6 @@ def library():
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 
@@ -391,6 +402,65 @@ def fa_bwd_dq(q, k, v, do, workspace, dq, scale=None, causal=False):
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
             ws_bytes, B, H, N, d, _dtype_code(q), _scale(scale, d),
             int(bool(causal)), _stream(q.device)))
+
+
+def fa_tile_grid(pass_, d, sparse=False):
+    """(rows, cols) of one pass's tiles in the bf16 kernels: pass 0 forward
+    (query tile x key tile), 1 dK/dV pass (query stage x key tile), 2 dQ
+    pass (query tile x key tile)."""
+    rows, cols = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(library().fa_tile_grid(int(pass_), int(d), int(bool(sparse)),
+                                  ctypes.byref(rows), ctypes.byref(cols)))
+    return rows.value, cols.value
+
+
+def fa_fwd_tile_visits(q, k, v, block_mask=None, block_m=128, block_n=128,
+                       scale=None, causal=False):
+    """fa_fwd_blocksparse (block_mask None: fa_fwd) through the counting
+    kernel instances: returns O, LSE and an int32 tensor B x H x Tq of the
+    key tiles each query tile visited."""
+    B, H, N, d = _shape4(q, k, v)
+    lib = library()
+    mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
+    rows, _ = fa_tile_grid(0, d, mask_t is not None)
+    visits = torch.full((B, H, -(-N // rows)), -1, dtype=torch.int32,
+                        device=q.device)
+    o, lse_t = _fwd_outputs(q, (B, H, N, d), None, None)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_tile_visits(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+            _dtype_code(q), _scale(scale, d), int(bool(causal)),
+            _ptr(mask_t), int(block_m), int(block_n), _ptr(visits),
+            visits.numel(), _stream(q.device)))
+    return o, lse_t, visits
+
+
+def fa_bwd_tile_visits(q, k, v, o, do, lse, block_mask=None, block_m=128,
+                       block_n=128, scale=None, causal=False):
+    """fa_bwd_blocksparse (block_mask None: fa_bwd) through the counting
+    kernel instances: returns dQ, dK, dV, the query stages each key tile of
+    the dK/dV pass visited (B x H x Tk) and the key tiles each query tile of
+    the dQ pass visited (B x H x Tq)."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    lib = library()
+    mask_t = _mask_arg(block_mask, N, block_m, block_n, q.device)
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    _, kv_cols = fa_tile_grid(1, d, mask_t is not None)
+    q_rows, _ = fa_tile_grid(2, d, mask_t is not None)
+    v_kv = torch.full((B, H, -(-N // kv_cols)), -1, dtype=torch.int32,
+                      device=q.device)
+    v_q = torch.full((B, H, -(-N // q_rows)), -1, dtype=torch.int32,
+                     device=q.device)
+    dq, dk, dv = _grads(q, None, None, None)
+    ws, ws_bytes = _workspace(B, H, N, d, q.device, None)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_tile_visits(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, B, H, N, d, _dtype_code(q),
+            _scale(scale, d), int(bool(causal)), _ptr(mask_t), int(block_m),
+            int(block_n), _ptr(v_kv), v_kv.numel(), _ptr(v_q), v_q.numel(),
+            _stream(q.device)))
+    return dq, dk, dv, v_kv, v_q
 
 
 # Short names for the common calls (the same functions).

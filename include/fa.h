@@ -282,6 +282,55 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                     int64_t d, fa_dtype dt, float scale, int causal,
                     void* stream);
 
+/*
+ * Diagnostics: the tile schedule of the bf16 kernels.  The causal rule
+ * visits, for a block of queries, only the key blocks at or before its last
+ * query ([REAPER], causal-mask question: with T square blocks per side,
+ * T(T+1)/2 of the T^2 blocks), and the block-sparse forms only the blocks
+ * whose mask entry is nonzero ([XYZ], section "Block-Sparse
+ * FlashAttention").  These calls report what the kernels actually visited.
+ *
+ * fa_tile_grid — rows x cols of one pass's tiles, for head dim d (64 or 128)
+ *   and the dense (sparse = 0) or block-sparse (sparse != 0) instances:
+ *     pass 0, forward:     query tile rows x key tile keys;
+ *     pass 1, dK/dV pass:  query stage rows x key tile keys (a workgroup owns
+ *                          one key tile and visits query stages);
+ *     pass 2, dQ pass:     query tile rows x key tile keys.
+ *   FA_ERR_ARG for another pass, FA_ERR_UNSUPPORTED for another d,
+ *   FA_ERR_NULL for a NULL output.
+ *
+ * fa_fwd_tile_visits — exactly fa_fwd_blocksparse (mask == NULL: fa_fwd),
+ *   same kernel and results, and in addition, for head bh = b*H + h and
+ *   query tile i (pass 0 grid, Tq = ceil(N / rows) tiles per head),
+ *   visits[bh * Tq + i] = the number of key tiles the kernel visited.
+ *   visits: device int32 buffer of visits_len >= B*H*Tq elements (else
+ *   FA_ERR_ARG), 4-byte aligned.  FA_BF16 only (else FA_ERR_UNSUPPORTED).
+ *
+ * fa_bwd_tile_visits — exactly fa_bwd_blocksparse (mask == NULL: fa_bwd),
+ *   and in addition visits_kv[bh * Tk + j] = query stages visited by key
+ *   tile j in the dK/dV pass (pass 1 grid, Tk = ceil(N / cols)) and
+ *   visits_q[bh * Tq + i] = key tiles visited by query tile i in the dQ
+ *   pass (pass 2 grid, Tq = ceil(N / rows)).  Lengths, alignment and dtype
+ *   as fa_fwd_tile_visits.
+ */
+fa_status fa_tile_grid(int pass, int64_t d, int sparse, int64_t* rows,
+                       int64_t* cols);
+fa_status fa_fwd_tile_visits(const void* q, const void* k, const void* v,
+                             void* o, float* lse, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, int32_t* visits,
+                             size_t visits_len, void* stream);
+fa_status fa_bwd_tile_visits(const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, fa_dtype dt, float scale,
+                             int causal, const uint8_t* mask, int64_t block_m,
+                             int64_t block_n, int32_t* visits_kv,
+                             size_t kv_len, int32_t* visits_q, size_t q_len,
+                             void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

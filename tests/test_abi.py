@@ -24,6 +24,9 @@ MISALIGNED = 0x10008
 @pytest.fixture(scope="module")
 def lib():
     from exact_io_aware_amd import _build, fa
+    alt = os.environ.get("FA_ABI_TEST_LIB")
+    if alt:  # the host-only sanitizer build (tests/test_abi_sanitized.py)
+        return fa.declare(ctypes.CDLL(alt))
     if not os.path.exists(_build.LIB_PATH):
         _build.build()
     return fa.library()
@@ -302,3 +305,46 @@ def test_binding_short_names():
     from exact_io_aware_amd import fa
     assert fa.fwd is fa.fa_fwd and fa.bwd is fa.fa_bwd
     assert callable(fa.fwd_blocksparse)
+
+
+def test_tile_grid(lib):
+    """The tile grids of the bf16 kernels (a host-side query, no GPU)."""
+    from exact_io_aware_amd import fa
+    assert fa.fa_tile_grid(0, 128) == (256, 64)
+    assert fa.fa_tile_grid(0, 64) == (128, 128)
+    assert fa.fa_tile_grid(0, 128, sparse=True) == (128, 64)
+    assert fa.fa_tile_grid(1, 128) == (64, 128)
+    assert fa.fa_tile_grid(1, 64) == (128, 128)
+    assert fa.fa_tile_grid(2, 128) == (256, 64)
+    assert fa.fa_tile_grid(2, 128, sparse=True) == (128, 64)
+    assert fa.fa_tile_grid(2, 64) == (128, 128)
+    r, c = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.fa_tile_grid(3, 128, 0, ctypes.byref(r), ctypes.byref(c)) == FA_ERR_ARG
+    assert lib.fa_tile_grid(0, 96, 0, ctypes.byref(r), ctypes.byref(c)) == FA_ERR_UNSUPPORTED
+    assert lib.fa_tile_grid(0, 128, 0, None, ctypes.byref(c)) == FA_ERR_NULL
+
+
+def test_tile_visits_validation(lib):
+    """The counting calls validate as the plain calls, plus their count
+    buffers (NULL, alignment, length) and the dtype (bf16 only)."""
+    def fwdv(visits=P, n_vis=1 << 20, dt=BF16, B=1, H=2, N=1000, d=128,
+             mask=None, q=P):
+        return lib.fa_fwd_tile_visits(q, P, P, P, P, B, H, N, d, dt, 0.1, 1,
+                                      mask, 128, 128, visits, n_vis, None)
+    assert fwdv(dt=F32) == FA_ERR_UNSUPPORTED
+    assert fwdv(visits=None) == FA_ERR_NULL
+    assert fwdv(visits=P + 2) == FA_ERR_ALIGN
+    assert fwdv(n_vis=2 * 4 - 1) == FA_ERR_ARG       # 2 heads x 4 tiles of 256
+    assert fwdv(q=None) == FA_ERR_NULL
+    assert fwdv(B=0, visits=None) == FA_OK
+
+    def bwdv(vkv=P, nkv=1 << 20, vq=P, nq=1 << 20, dt=BF16, ws=1 << 20):
+        return lib.fa_bwd_tile_visits(P, P, P, P, P, P, P, P, P, P, ws, 1, 2,
+                                      1000, 128, dt, 0.1, 1, None, 128, 128,
+                                      vkv, nkv, vq, nq, None)
+    assert bwdv(dt=F32) == FA_ERR_UNSUPPORTED
+    assert bwdv(vkv=None) == FA_ERR_NULL
+    assert bwdv(vq=P + 1) == FA_ERR_ALIGN
+    assert bwdv(nkv=2 * 8 - 1) == FA_ERR_ARG        # 2 heads x 8 key tiles
+    assert bwdv(nq=2 * 4 - 1) == FA_ERR_ARG         # 2 heads x 4 query tiles
+    assert bwdv(ws=16) == FA_ERR_ARG
