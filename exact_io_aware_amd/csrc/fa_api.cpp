@@ -403,6 +403,41 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
   return from_hip(run_dq(a, dt, s));
 }
 
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, int64_t B,
+                         int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                         float scale, int causal, void* stream) {
+  {
+    bool empty = false;
+    int64_t bh = 0;
+    fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
+    if (st != FA_OK) return st;
+    if (!empty && ws_bytes(bh, N) > fa::noalloc_scratch_bytes()) {
+      return FA_ERR_SCRATCH;
+    }
+  }
+  // Validate every argument as fa_bwd does, with an aligned stand-in for the
+  // workspace pointer (never dereferenced); the real address comes after.
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            stand_in, fa::noalloc_scratch_bytes(), B, H, N,
+                            d, dt, scale, true, causal, &a, &empty);
+  if (st != FA_OK || empty) return st;
+  void* ws = nullptr;
+  if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  a.ws_d = static_cast<float*>(ws);
+  a.ws_lse2 = a.ws_d + ws_rows(a.bh, N);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(run_pre(a, dt, s));
+  if (st != FA_OK) return st;
+  st = from_hip(run_dkdv(a, dt, s));
+  if (st != FA_OK) return st;
+  return from_hip(run_dq(a, dt, s));
+}
+
 fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
                          const void* o, const void* dout, const float* lse,
                          float* dq, float* dk, float* dv, void* workspace,
@@ -530,6 +565,9 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_ARG:
       return "FA_ERR_ARG: scale must be finite and > 0, workspace large enough, "
              "drop probability in [0, 255/256]";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: problem exceeds the library's fixed scratch "
+             "(fa_bwd_noalloc needs B*H*N <= 2^20 rows)";
   }
   return "unknown fa_status";
 }

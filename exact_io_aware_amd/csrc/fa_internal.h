@@ -98,4 +98,10 @@ void fwd_bf16_tile_grid(int d, bool sparse, int* rows, int* cols);
 void bwd_dkdv_tile_grid(int d, int* rows, int* cols);
 void bwd_dq_tile_grid(int d, bool sparse, int* rows, int* cols);
 
+// Library-owned scratch of the entry points that allocate nothing
+// (fa_noalloc.hip): its size, and its device address on the current device
+// (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace fa

@@ -18,7 +18,7 @@ from . import _build
 __all__ = [
     "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv",
     "fa_fwd_splitkv_chunks", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-    "fa_bwd_blocksparse", "fa_bwd_preprocess",
+    "fa_bwd_blocksparse", "fa_bwd_noalloc", "fa_bwd_preprocess",
     "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
     "fa_tile_grid", "fa_fwd_tile_visits", "fa_bwd_tile_visits",
     "fa_version", "library", "LIB_PATH",
@@ -75,6 +75,8 @@ def declare(lib):
                            P],
         "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
                            I64, I, F, I, F, U64, P],
+        "fa_bwd_noalloc": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I,
+                           F, I, P],
         "fa_tile_grid": [I, I64, I, P, P],
         "fa_fwd_tile_visits": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
                                I64, I64, P, SZ, P],
@@ -313,6 +315,25 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, workspace=None,
                           ws_bytes, B, H, N, d, _dtype_code(q),
                           _scale(scale, d), int(bool(causal)),
                           _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None,
+                   causal=False):
+    """fa_bwd without a workspace: the library's own scratch holds the
+    per-row values (B*H*N <= 2^20).  The caller passes the output tensors
+    dq, dk, dv (float32, q's shape); nothing is allocated."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    lib = library()
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _arg(t, name, q.shape, torch.float32, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), B, H, N, d, _dtype_code(q),
+                                  _scale(scale, d), int(bool(causal)),
+                                  _stream(q.device)))
     return dq, dk, dv
 
 

@@ -24,9 +24,10 @@
  *   B x H x N float32 arrays in the same (b, h, i) order.  Queries and keys
  *   have the same length N (except in fa_fwd_splitkv).
  * Pointers.  Every tensor pointer is a device pointer owned by the caller,
- *   aligned to 16 bytes.  The library allocates no device memory and keeps no
- *   mutable global state; concurrent calls on different streams are safe as
- *   long as their output buffers do not overlap.
+ *   aligned to 16 bytes.  The library allocates no device memory; its only
+ *   global state is the per-device address of the scratch array of
+ *   fa_bwd_noalloc.  Concurrent calls on different streams are safe as long
+ *   as their output buffers do not overlap (fa_bwd_noalloc: see there).
  * Stream.  `stream` is a hipStream_t passed as void* (NULL = the null
  *   stream).  Work is enqueued and the call returns without synchronising;
  *   outputs are valid once the stream has reached that point.
@@ -64,6 +65,8 @@ typedef enum {
   FA_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned        */
   FA_ERR_ARG = 8,         /* scale not finite and > 0, workspace too small,
                              drop probability out of range                 */
+  FA_ERR_SCRATCH = 9,     /* problem larger than the library's fixed scratch
+                             (fa_bwd_noalloc)                              */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -251,6 +254,31 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v,
                          int64_t N, int64_t d, fa_dtype dt, float scale,
                          int causal, float p_drop, uint64_t seed,
                          void* stream);
+
+/*
+ * fa_bwd_noalloc — fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same three kernels and results (bitwise equal to fa_bwd),
+ * with the per-row workspace taken from a scratch array that the library
+ * holds in device memory instead of from the caller.  The caller still
+ * passes every input and output.  The call allocates nothing and frees
+ * nothing (its first call on a device looks up that device's copy of the
+ * array, which lives until the process ends).
+ *
+ * Limit: B*H*N <= 2^20 rows (the scratch holds two float arrays of 2^20
+ * rows, 8 MiB); larger problems return FA_ERR_SCRATCH before any HIP call.
+ * Nothing in the scratch needs to start at zero: the row pass writes every
+ * row the gradient passes read.  All calls on one GPU share that GPU's
+ * scratch and it keeps the last call's contents, so calls that overlap in
+ * time on one GPU (different streams, or different host threads) race;
+ * serialise them.  The stream must belong to the current device.
+ * Arguments, outputs and other errors as fa_bwd.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, int64_t B,
+                         int64_t H, int64_t N, int64_t d, fa_dtype dt,
+                         float scale, int causal, void* stream);
 
 /* Bytes of workspace fa_bwd and fa_bwd_blocksparse need (0 for empty
  * problems). */

@@ -14,6 +14,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE = 0, 1, 2, 3
 FA_ERR_UNSUPPORTED, FA_ERR_MASK, FA_ERR_HIP, FA_ERR_ALIGN, FA_ERR_ARG = (
     4, 5, 6, 7, 8)
+FA_ERR_SCRATCH = 9
 F32, BF16 = 0, 1
 
 # Fake, aligned, never-dereferenced device addresses.
@@ -47,7 +48,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.fa_version()
-    for code in range(9):
+    for code in range(10):
         assert lib.fa_status_str(code).startswith(b"FA_")
     assert lib.fa_status_str(99) == b"unknown fa_status"
 
@@ -305,6 +306,29 @@ def test_binding_short_names():
     from exact_io_aware_amd import fa
     assert fa.fwd is fa.fa_fwd and fa.bwd is fa.fa_bwd
     assert callable(fa.fwd_blocksparse)
+
+
+def test_bwd_noalloc_validation(lib):
+    """fa_bwd_noalloc checks as fa_bwd does, and rejects problems larger
+    than its fixed scratch (B*H*N > 2^20 rows) with FA_ERR_SCRATCH, all
+    before any HIP call."""
+    def call(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2,
+             N=128, d=64, dt=BF16, scale=0.125, causal=1):
+        return lib.fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N,
+                                  d, dt, scale, causal, None)
+    assert call(B=1, H=1, N=(1 << 20) + 1) == FA_ERR_SCRATCH
+    assert call(B=2, H=32, N=16384 + 1) == FA_ERR_SCRATCH
+    assert call(B=1, H=64, N=(1 << 14) + 64, q=None) == FA_ERR_SCRATCH
+    assert call(B=-1) == FA_ERR_SHAPE
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(dt=5) == FA_ERR_DTYPE
+    assert call(scale=float("nan")) == FA_ERR_ARG
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call(**{name: None}) == FA_ERR_NULL, name
+    assert call(dk=MISALIGNED) == FA_ERR_ALIGN
+    for B, H, N in ((0, 4, 128), (2, 0, 128), (2, 4, 0)):
+        assert call(q=None, k=None, v=None, o=None, do=None, lse=None,
+                    dq=None, dk=None, dv=None, B=B, H=H, N=N) == FA_OK
 
 
 def test_tile_grid(lib):
