@@ -245,13 +245,35 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     adk[db] = zero16();
     adv[db] = zero16();
   }
-  int aoff[T::KS];  // row-wise operand: row l32 (+ 32-row block), chunk ks*2 + h
+  // Per-lane LDS offsets with this wave's fixed parts (its key block kw and
+  // query half qh) folded in, so that every LDS read below is one register
+  // plus an immediate offset under 64 KB (the stage parity, the block within
+  // the stage and the Q / dO or K / V choice).
+  //   aK: row-wise K (and, + OFF_V, V) operand: row kw*32 + l32, chunk ks*2 + h;
+  //   aQ: row-wise Q (and, + S_DO, dO) operand of the wave's first query block
+  //       in stage 0;
+  //   aT: transposed reads of that block (slots 0-3 / 4-7, see tr_offsets);
+  //   aL: this half-wave's lse2 entries of that block (+ S_D - S_L: D).
+  //   (At d = 64 aQ is aK plus a wave-uniform difference, one add per
+  //   read, which keeps the causal instance within its registers.)
+  constexpr bool OWN_AQ = (D == 128);
+  int aK[T::KS], aQ[OWN_AQ ? T::KS : 1];
+  const int q_minus_k = T::OFF_ST + qh * T::QBW * 32 * T::ROW - kw * 32 * T::ROW;
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) aoff[ks] = tile_off<D>(l32, ks * 2 + h);
-  int toff[T::DB][2];
-  tr_offsets<D, T::DB>(lane, toff);
-  const unsigned char* sk = smem + kw * 32 * T::ROW;
-  const unsigned char* sv = smem + T::OFF_V + kw * 32 * T::ROW;
+  for (int ks = 0; ks < T::KS; ++ks) {
+    const int o = tile_off<D>(l32, ks * 2 + h);
+    aK[ks] = kw * 32 * T::ROW + o;
+    if constexpr (OWN_AQ) aQ[ks] = aK[ks] + q_minus_k;
+  }
+  auto a_q = [&](int ks) { return OWN_AQ ? aQ[OWN_AQ ? ks : 0] : aK[ks] + q_minus_k; };
+  int aT[T::DB][2];
+  tr_offsets<D, T::DB>(lane, aT);
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    aT[db][0] += T::OFF_ST + qh * T::QBW * 32 * T::ROW;
+    aT[db][1] += T::OFF_ST + qh * T::QBW * 32 * T::ROW;
+  }
+  const int aL = T::OFF_ST + T::S_L + (qh * T::QBW * 32 + h * 4) * 4;
 
   // Block-sparse: the query tiles whose mask block in this workgroup's key
   // column is nonzero (a 64-row tile lies in one 128-multiple block row).
@@ -284,9 +306,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     wait_dma();
     __syncthreads();
     if (qt_next < n_qt) issue_stage(qt_next, stage ^ 1);
-    const unsigned char* st = smem + T::OFF_ST + stage * T::STAGE;
-    const float* sL = reinterpret_cast<const float*>(st + T::S_L);
-    const float* sD = reinterpret_cast<const float*>(st + T::S_D);
+    const int so = stage * T::STAGE;  // immediate when the parity is static
 #pragma unroll
     for (int qi = 0; qi < T::QBW; ++qi) {
       const int qb = qh * T::QBW + qi;
@@ -300,9 +320,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
-        const unsigned char* pa = st + qb * 32 * T::ROW + aoff[ks];
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(sk + aoff[ks]);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sv + aoff[ks]);
+        const unsigned char* pa = smem + a_q(ks) + so + qi * 32 * T::ROW;
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(smem + aK[ks]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + T::OFF_V + aK[ks]);
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
       }
@@ -313,8 +333,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       const int qhi = n - qq0 - h * 4;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(sL + qb * 32 + g * 8 + h * 4);
-        const f32x4 Dv = *reinterpret_cast<const f32x4*>(sD + qb * 32 + g * 8 + h * 4);
+        const unsigned char* pl = smem + aL + so + (qi * 32 + g * 8) * 4;
+        const f32x4 L = *reinterpret_cast<const f32x4*>(pl);
+        const f32x4 Dv = *reinterpret_cast<const f32x4*>(pl + (T::S_D - T::S_L));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
@@ -339,13 +360,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // transposed operands come from transpose reads of the Q / dO tiles.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const unsigned char* pk = st + (qb * 2 + s2) * 16 * T::ROW;
+        const int pk = so + (qi * 2 + s2) * 16 * T::ROW;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
-          const bf16x8 a_do = join_tr16(lds_read_tr16(pk + T::S_DO + toff[db][0]),
-                                        lds_read_tr16(pk + T::S_DO + toff[db][1]));
-          const bf16x8 a_q = join_tr16(lds_read_tr16(pk + toff[db][0]),
-                                       lds_read_tr16(pk + toff[db][1]));
+          const bf16x8 a_do = join_tr16(lds_read_tr16(smem + aT[db][0] + pk + T::S_DO),
+                                        lds_read_tr16(smem + aT[db][1] + pk + T::S_DO));
+          const bf16x8 a_q = join_tr16(lds_read_tr16(smem + aT[db][0] + pk),
+                                       lds_read_tr16(smem + aT[db][1] + pk));
           adv[db] = mfma32(a_do, pf[s2], adv[db]);
           adk[db] = mfma32(a_q, sf[s2], adk[db]);
         }
