@@ -676,6 +676,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           adq[db] = mfma32(a, sf[s2], adq[db]);
         }
       }
+      // One 32-key block at a time: its score registers are free before the
+      // next block's products, room the scheduler uses to keep two LDS
+      // operands in flight.
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
