@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv_kernel": ["fa_bwd_bf16.hip"],
     "bwd_dq_kernel": ["fa_bwd_bf16.hip"],
     "splitkv_bf16_kernel": ["fa_fwd_bf16.hip"],
+    "bwd_blocksparse": ["fa_bwd_bf16.hip"],
 }
 
 
@@ -69,18 +70,30 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel, workload):
-    """HBM bytes per launch from a committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
+def _stored(kernel, workload, key):
+    """A value `key: number` from the committed counter summary of a kernel
+    on a workload, or None when there is none or the kernel sources changed
+    since the counters were taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_b = re.search(key + r":\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
     if not m_b or not m_h or m_h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_b.group(1))
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)."""
+    return _stored(kernel, workload, "traffic_bytes_per_launch")
+
+
+def stored_clock_ghz(kernel, workload):
+    """The engine clock while the kernel ran: GRBM_GUI_ACTIVE cycles per XCD
+    over the kernel's duration, from the same counter summary."""
+    return _stored(kernel, workload, "gpu_clock_ghz")
 
 
 def calib_copy(mb):
@@ -104,6 +117,9 @@ def time_workload(name, steps, warmup, calib_mb=0):
     dev = torch.device("cuda:0")
     x = workloads.workload_inputs(name, with_do=True, device=dev)
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    if w["dtype"] != "bf16":
+        raise SystemExit(f"{name}: the step bench times bf16 workloads "
+                         "(--all covers the fp32 ones)")
     scale = w["scale"]
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
@@ -116,7 +132,32 @@ def time_workload(name, steps, warmup, calib_mb=0):
     if calib_mb:
         calib_copy(calib_mb)
 
-    names = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    mask = workloads.workload_mask(w)
+    mask_t = torch.from_numpy(mask).to(dev) if mask is not None else None
+    has_bwd = "bwd" in w["passes"]
+    # The step's calls, each timed: dense backward workloads call the three
+    # backward passes one by one; the block-sparse workload its forward and
+    # its whole backward; forward-only workloads every causal mode they list.
+    if mask_t is not None:
+        calls = [("fwd", lambda: fa.fa_fwd_blocksparse(
+                     q, k, v, mask_t, scale=scale, causal=causal, out=o, lse=lse)),
+                 ("bwd", lambda: fa.fa_bwd_blocksparse(
+                     q, k, v, o, do, lse, mask_t, scale=scale, causal=causal,
+                     workspace=ws, dq=dq, dk=dk, dv=dv))]
+    elif has_bwd:
+        calls = [("fwd", lambda: fa.fa_fwd(q, k, v, scale=scale, causal=causal,
+                                           out=o, lse=lse)),
+                 ("bwd_preprocess", lambda: fa.fa_bwd_preprocess(o, do, lse, ws)),
+                 ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv,
+                                                     scale=scale, causal=causal)),
+                 ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, ws, dq, scale=scale,
+                                                 causal=causal))]
+    else:
+        calls = [("fwd" if c else "fwd_noncausal",
+                  (lambda c=c: fa.fa_fwd(q, k, v, scale=scale, causal=c, out=o,
+                                         lse=lse)))
+                 for c in w["causal"]]
+    names = tuple(n for n, _ in calls)
     ev = {n: [] for n in names}
 
     def rec():
@@ -126,18 +167,11 @@ def time_workload(name, steps, warmup, calib_mb=0):
 
     def step(record):
         marks = [rec()] if record else None
-        fa.fa_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        for _, call in calls:
+            call()
+            if record:
+                marks.append(rec())
         if record:
-            marks.append(rec())
-        fa.fa_bwd_preprocess(o, do, lse, ws)
-        if record:
-            marks.append(rec())
-        fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale=scale, causal=causal)
-        if record:
-            marks.append(rec())
-        fa.fa_bwd_dq(q, k, v, do, ws, dq, scale=scale, causal=causal)
-        if record:
-            marks.append(rec())
             for i, n in enumerate(names):
                 ev[n].append((marks[i], marks[i + 1]))
 
@@ -154,18 +188,26 @@ def time_workload(name, steps, warmup, calib_mb=0):
     ms_step = t0.elapsed_time(t1) / steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / steps
                for n in names}
-    ff = fwd_flops(B, H, N, d, causal)
-    alg = {"fwd": ff, "bwd_preprocess": 0.0, "bwd_dkdv": 0.8 * 2.5 * ff,
-           "bwd_dq": 0.2 * 2.5 * ff}
+    if mask is not None:
+        ff = 4.0 * d * 128 * 128 * float(mask.sum()) * B * H
+    else:
+        ff = fwd_flops(B, H, N, d, causal)
+    alg = {"fwd": ff, "fwd_noncausal": fwd_flops(B, H, N, d, False),
+           "bwd": 2.5 * ff, "bwd_preprocess": 0.0,
+           "bwd_dkdv": 0.8 * 2.5 * ff, "bwd_dq": 0.2 * 2.5 * ff}
+    alg = {n: alg[n] for n in names}
     return dict(w=w, B=B, H=H, N=N, d=d, causal=causal, ms_step=ms_step,
-                wall=wall, kern_ms=kern_ms, fwd_flops=ff, bwd_flops=2.5 * ff,
-                alg=alg)
+                wall=wall, kern_ms=kern_ms, fwd_flops=ff,
+                bwd_flops=2.5 * ff if has_bwd else 0.0, alg=alg,
+                step_flops=sum(alg.values()), sparse=mask is not None)
 
 
-def time_passes(name, steps, warmup):
+def time_passes(name, steps, warmup, oracle_check=False):
     """Per-workload timing of every pass the workload lists (used by --all):
     the forward, and for workloads with a backward the whole fa_bwd (or
-    fa_bwd_blocksparse) call, inputs O and LSE from the forward (untimed)."""
+    fa_bwd_blocksparse) call, inputs O and LSE from the forward (untimed).
+    With oracle_check each line also carries the parity and the oracle's
+    throughput on a sample of whole heads (parity_and_baseline)."""
     import torch
 
     from exact_io_aware_amd import fa, workloads
@@ -234,12 +276,90 @@ def time_passes(name, steps, warmup):
         for pname, run, fl in passes:
             ms = median_ms(run)
             tf = fl / (ms * 1e-3) / 1e12
-            res = dict(workload=name, causal=causal, pass_=pname,
+            res = dict(workload=name, causal=causal, **{"pass": pname},
                        ms_median=ms, tflops=tf, frac_peak=tf / peak)
             if p_drop:
                 res["p_drop"] = p_drop
+            if oracle_check:
+                got = run()
+                torch.cuda.synchronize()
+                if pname == "bwd":
+                    got = grads
+                res.update(parity_and_baseline(w, x, causal, mask, pname, got,
+                                               fl))
             out.append(res)
     return out
+
+
+def parity_and_baseline(w, x, causal, mask, pname, got, flops):
+    """The fp64 oracle on a bounded sample of whole heads of a workload:
+    parity of the GPU outputs on those heads (max-abs and relative RMS over
+    the sampled heads, against the bars: fp32 max-abs 1e-5; bf16 max-abs
+    2e-2 (x 256/(256-t) with dropout) and rel-RMS 5e-3), and the oracle's
+    own throughput on them (the same algorithmic FLOP per head as the GPU
+    line; it materialises the full N^2 even where causal)."""
+    import numpy as np
+
+    import oracle
+
+    B, H = w["B"], w["H"]
+    heads = [(0, 0)] if (B, H) == (1, 1) else [(0, 0), (B - 1, H - 1)]
+    if w["N"] >= 16384:
+        heads = heads[:1]
+    f64 = lambda t: t.detach().double().cpu().numpy()  # noqa: E731
+    names = ("O", "LSE") if pname == "fwd" else ("dQ", "dK", "dV")
+    errs = {n: [0.0, 0.0, 0.0] for n in names}  # max-abs, sum sq diff, sum sq ref
+    t_cpu = 0.0
+    p_drop = w.get("p_drop", 0.0)
+    t_drop = oracle.dropout_threshold(p_drop) if p_drop else 0
+    for b, h in heads:
+        q, k, v = (f64(x[n][b, h]) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        if pname == "fwd":
+            if p_drop:
+                ref = oracle.attention_fwd_dropout_head(
+                    q, k, v, w["scale"], causal, t_drop, w["drop_seed"],
+                    b * H + h)
+            else:
+                ref = oracle.attention_fwd_head(q, k, v, w["scale"], causal,
+                                                mask, 128, 128)
+        else:
+            do = f64(x["do"][b, h])
+            if p_drop:
+                ref = oracle.attention_bwd_dropout_head(
+                    q, k, v, do, w["scale"], causal, t_drop, w["drop_seed"],
+                    b * H + h)
+            else:
+                ref = oracle.attention_bwd_head(q, k, v, do, w["scale"],
+                                                causal, mask, 128, 128)
+        t_cpu += time.perf_counter() - t0
+        for n, g, r in zip(names, got, ref):
+            g = f64(g[b, h])
+            ok = ~np.isneginf(r)
+            d_ = g[ok] - r[ok]
+            e = errs[n]
+            e[0] = max(e[0], float(np.max(np.abs(d_))) if d_.size else 0.0)
+            e[1] += float(np.sum(d_ * d_))
+            e[2] += float(np.sum(r[ok] * r[ok]))
+    fp32 = w["dtype"] == "f32"
+    bar_abs = 1e-5 if fp32 else 2e-2 * 256.0 / (256 - t_drop)
+    parity, passed = {}, True
+    for n, (mx, sd, sr) in errs.items():
+        rel = (sd / sr) ** 0.5 if sr > 0 else 0.0
+        ok = mx <= bar_abs and (fp32 or rel <= 5e-3)
+        passed &= ok
+        parity[n] = {"max_abs": mx, "rel_rms": rel}
+    head_flops = flops / (B * H) * len(heads)
+    return {
+        "parity": dict(parity, heads=[list(hh) for hh in heads],
+                       max_abs_bar=bar_abs, rel_rms_bar=None if fp32 else 5e-3,
+                       passed=passed),
+        "cpu_baseline": {
+            "value": head_flops / t_cpu / 1e12, "unit": "TFLOP/s",
+            "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": (f"{len(heads)} whole head(s) {heads}, fp64 NumPy, "
+                       f"full N^2 materialised, {t_cpu:.2f} s")},
+    }
 
 
 def decode_bytes(w, Nq=None):
@@ -250,7 +370,7 @@ def decode_bytes(w, Nq=None):
                               + 4 * Nq)
 
 
-def time_decode(name, steps, warmup, keep=None):
+def time_decode(name, steps, warmup, keep=None, oracle_check=False):
     """Timing of the split-KV forward on a decoding workload (used by --all):
     the whole fa_fwd_splitkv call (chunk pass + merge), median over steps.
     The work is a matrix-vector product per head, bound by HBM bandwidth, so
@@ -291,11 +411,49 @@ def time_decode(name, steps, warmup, keep=None):
         ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
         nbytes = decode_bytes(w)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        out.append(dict(workload=name, causal=causal, pass_="decode",
-                        ms_median=ms, gbytes_per_s=gbs,
-                        frac_hbm_peak=gbs / PEAK_HBM_GBS,
-                        chunks=fa.fa_fwd_splitkv_chunks(B, H, Nq, Nk, d, 0)))
+        res = dict(workload=name, causal=causal, **{"pass": "decode"},
+                   ms_median=ms, gbytes_per_s=gbs,
+                   frac_hbm_peak=gbs / PEAK_HBM_GBS,
+                   chunks=fa.fa_fwd_splitkv_chunks(B, H, Nq, Nk, d, 0))
+        if oracle_check:
+            res.update(decode_parity(w, x, causal, o, lse))
+        out.append(res)
     return out
+
+
+def decode_parity(w, x, causal, o, lse, heads=((0, 0), (-1, -1))):
+    """The decoding oracle on two whole heads: parity (bf16 bars) and its
+    throughput in GB/s of the same algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+
+    f64 = lambda t: t.detach().double().cpu().numpy()  # noqa: E731
+    errs = {"O": [0.0, 0.0, 0.0], "LSE": [0.0, 0.0, 0.0]}
+    t_cpu = 0.0
+    for b, h in heads:
+        q, k, v = (f64(x[n][b, h]) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        ref = oracle.attention_decode_head(q, k, v, w["scale"], causal)
+        t_cpu += time.perf_counter() - t0
+        for n, g, r in zip(("O", "LSE"), (o, lse), ref):
+            d_ = f64(g[b, h]) - r
+            e = errs[n]
+            e[0] = max(e[0], float(np.max(np.abs(d_))))
+            e[1] += float(np.sum(d_ * d_))
+            e[2] += float(np.sum(r * r))
+    parity, passed = {}, True
+    for n, (mx, sd, sr) in errs.items():
+        rel = (sd / sr) ** 0.5 if sr > 0 else 0.0
+        passed &= mx <= 2e-2 and rel <= 5e-3
+        parity[n] = {"max_abs": mx, "rel_rms": rel}
+    per_head = decode_bytes(w) / (w["B"] * w["H"])
+    return {"parity": dict(parity, heads=[list(hh) for hh in heads],
+                           max_abs_bar=2e-2, rel_rms_bar=5e-3, passed=passed),
+            "cpu_baseline": {"value": per_head * len(heads) / t_cpu / 1e9,
+                             "unit": "GB/s", "cores": int(_blas_threads()),
+                             "kind": "oracle",
+                             "sample": f"{len(heads)} whole heads, fp64 NumPy, {t_cpu:.3f} s"}}
 
 
 def cpu_baseline(name, budget_s=12.0, max_heads=8):
@@ -309,26 +467,35 @@ def cpu_baseline(name, budget_s=12.0, max_heads=8):
     w = workloads.workload(name)
     x = workloads.workload_inputs(name, with_do=True)
     causal = w["causal"][-1]
+    mask = workloads.workload_mask(w)
+    has_bwd = "bwd" in w["passes"]
     heads, t_total = 0, 0.0
     for b in range(w["B"]):
         for hh in range(w["H"]):
             q, k, v, do = (x[n][b, hh].double().numpy() for n in
                            ("q", "k", "v", "do"))
             t0 = time.perf_counter()
-            oracle.attention_fwd_head(q, k, v, w["scale"], causal)
-            oracle.attention_bwd_head(q, k, v, do, w["scale"], causal)
+            oracle.attention_fwd_head(q, k, v, w["scale"], causal, mask)
+            if has_bwd:
+                oracle.attention_bwd_head(q, k, v, do, w["scale"], causal,
+                                          mask)
             t_total += time.perf_counter() - t0
             heads += 1
             if t_total >= budget_s or heads >= max_heads:
                 break
         if t_total >= budget_s or heads >= max_heads:
             break
-    flops = 3.5 * fwd_flops(1, 1, w["N"], w["d"], causal) * heads
+    if mask is not None:
+        head_fwd = 4.0 * w["d"] * 128 * 128 * float(mask.sum())
+    else:
+        head_fwd = fwd_flops(1, 1, w["N"], w["d"], causal)
+    flops = (3.5 if has_bwd else 1.0) * head_fwd * heads
+    what = "forward + backward" if has_bwd else "forward"
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
-            "sample": (f"{heads} whole heads (b,h) of {name}, forward + "
-                       f"backward, fp64 NumPy materialising S and P "
-                       f"(full N^2 even where causal), {t_total:.1f} s")}
+            "sample": (f"{heads} whole heads (b,h) of {name}, {what}, fp64 "
+                       f"NumPy materialising S and P (full N^2 even where "
+                       f"causal or masked), {t_total:.1f} s")}
 
 
 def cpu_baseline_decode(name, x, budget_s=12.0, max_heads=512):
@@ -451,16 +618,22 @@ def main():
     r = time_workload(args.workload, args.steps, args.warmup,
                       args.calib_copy_mb)
     B, H, N, d = r["B"], r["H"], r["N"], r["d"]
-    step_flops = r["fwd_flops"] + r["bwd_flops"]
+    step_flops = r["step_flops"]
     value = step_flops / (r["ms_step"] * 1e-3) / 1e12
     km = r["kern_ms"]
     fwd_tf = r["fwd_flops"] / (km["fwd"] * 1e-3) / 1e12
-    bwd_ms = km["bwd_preprocess"] + km["bwd_dkdv"] + km["bwd_dq"]
-    bwd_tf = r["bwd_flops"] / (bwd_ms * 1e-3) / 1e12
-    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: km[n])
+    bwd_ms = sum(km[n] for n in km if n.startswith("bwd"))
+    bwd_tf = r["bwd_flops"] / (bwd_ms * 1e-3) / 1e12 if bwd_ms else 0.0
+    # The dominant kernel: the timed call with the most time (the block-sparse
+    # backward's three kernels are timed as one call, fa_bwd_blocksparse,
+    # reported as "bwd_blocksparse").
+    cands = [n for n in km if n != "bwd_preprocess"]
+    dom = max(cands, key=lambda n: km[n])
     achieved = r["alg"][dom] / (km[dom] * 1e-3) / 1e12
-    kname = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
-             "bwd_dq": "bwd_dq_kernel"}[dom]
+    kname = {"fwd": "fwd_bf16_kernel", "fwd_noncausal": "fwd_bf16_kernel",
+             "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+             "bwd": "bwd_blocksparse"}[dom]
+    step_name = "fwd+bwd" if r["bwd_flops"] else "+".join(km)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -475,7 +648,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d,
-                   "causal": bool(r["causal"]), "step": "fwd+bwd",
+                   "causal": bool(r["causal"]), "step": step_name,
+                   "block_sparse": r["sparse"],
                    "seed": r["w"]["seed"], "sigma": r["w"]["sigma"]},
         "fwd_tflops": round(fwd_tf, 2),
         "bwd_tflops": round(bwd_tf, 2),
@@ -494,19 +668,33 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # The same kernel against the dense bf16 peak at the clock the GPU ran
+    # it at (256 CUs x 4096 flop/clk x f), f from the kernel's committed
+    # counters (GRBM_GUI_ACTIVE per XCD over the kernel time).
+    f_ghz = stored_clock_ghz(kname, args.workload)
+    if f_ghz:
+        peak_f = 256 * 4096 * f_ghz * 1e9 / 1e12
+        line["roofline"]["clock_ghz"] = f_ghz
+        line["roofline"]["clock_source"] = (
+            f"GRBM_GUI_ACTIVE / kernel time, profiles/{kname}_{args.workload}_pmc.md")
+        line["roofline"]["peak_at_clock"] = round(peak_f, 1)
+        line["roofline"]["frac_measured_clock"] = round(achieved / peak_f, 4)
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.workload)
     if args.all:
         from exact_io_aware_amd import workloads
         for name in workloads.WORKLOADS:
-            for res in time_passes(name, max(args.steps, 20), 3):
+            for res in time_passes(name, max(args.steps, 20), 3,
+                                   oracle_check=not args.no_cpu_baseline):
                 print(json.dumps(res), flush=True)
         for name in workloads.CONTEXT_WORKLOADS:
-            for res in time_passes(name, max(args.steps, 20), 3):
+            for res in time_passes(name, max(args.steps, 20), 3,
+                                   oracle_check=not args.no_cpu_baseline):
                 print(json.dumps(res), flush=True)
         for name in workloads.DECODE_WORKLOADS:
-            for res in time_decode(name, max(args.steps, 20), 3):
+            for res in time_decode(name, max(args.steps, 20), 3,
+                                   oracle_check=not args.no_cpu_baseline):
                 print(json.dumps(res), flush=True)
     print(json.dumps(line), flush=True)
 
