@@ -541,8 +541,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Vh = V + hoff;
   drop.bh = (uint32_t)head;
 
-  // One query tile of 32 * NW rows.
-  auto run_tile = [&](int qt) {
+  // One query tile of 32 * NW rows; REV walks its key tiles from the
+  // diagonal down to key 0 instead of up.
+  auto run_tile = [&](int qt, auto rev_tag) {
+  constexpr bool REV = decltype(rev_tag)::value;
   const int q0 = qt * T::BRQ;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
@@ -632,7 +634,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     ++nvis;
     wait_dma();
     __syncthreads();
-    if (kt_next < kt_end) fill(kt_next, stage ^ 1);
+    if (kt_next >= 0 && kt_next < kt_end) fill(kt_next, stage ^ 1);
     const unsigned char* st = smem + stage * T::STAGE;
     const int kbase = kt * T::BCK;
     // Last visible key of this lane's row relative to the key in register 0
@@ -701,6 +703,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       kt = kn;
       stage ^= 1;
     }
+  } else if constexpr (REV) {
+    // Key tile kt sits in stage kt & 1 in either direction.  Downwards the
+    // tiles needing the element mask come first, then (from an odd tile
+    // on) unmasked pairs with static stage parity.
+    int kt = kt_end - 1;
+    if (kt >= 0) fill(kt, kt & 1);
+#pragma unroll 1
+    for (; kt >= 0 && (needs_mask(kt) || !(kt & 1));
+         kt = __builtin_amdgcn_readfirstlane(kt - 1)) {
+      tile(yes{}, par_rt{}, kt, kt & 1, kt - 1);
+    }
+#pragma unroll 1
+    for (; kt > 0; kt = __builtin_amdgcn_readfirstlane(kt - 2)) {
+      tile(no{}, par1{}, kt, 1, kt - 1);
+      tile(no{}, par0{}, kt - 1, 0, kt - 2);
+    }
   } else if (kt_end > 0) {
     fill(0, 0);
     // Tiles needing the element mask come last; unmasked tiles run in
@@ -737,10 +755,20 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   };
 
-  run_tile(qt_a);
-  if (PAIRS && qt_b >= 0) {
-    __syncthreads();  // every wave is done with the K/V stages
-    run_tile(qt_b);
+  // The second tile of a pair walks its keys downwards.  Tiles u and
+  // n_qtiles-1-u together hold n_qtiles+1 tiles' worth of keys for every pair,
+  // so at any time the workgroups of a head read one of two key tiles:
+  // first tiles at position t going up, second tiles at the common position
+  // (n_qtiles+1)*256 - t going down.  The re-reads of K and V then hit the
+  // XCD's L2 instead of HBM.
+  // (The dropout instance keeps the upward walk: the downward one would
+  // not fit its registers.)
+  run_tile(qt_a, std::false_type{});
+  if constexpr (PAIRS) {
+    if (qt_b >= 0) {
+      __syncthreads();  // every wave is done with the K/V stages
+      run_tile(qt_b, std::integral_constant<bool, !DROP>{});
+    }
   }
 }
 

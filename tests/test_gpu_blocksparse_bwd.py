@@ -1,7 +1,8 @@
 """GPU parity of the block-sparse backward (fa_bwd_blocksparse) against the
 fp64 oracle's masked gradients, plus the identities the mask fixes: an
-all-ones mask is the dense backward (bitwise: same tiles, same order), a
-diagonal mask is the dense backward of each diagonal chunk, and queries
+all-ones mask is the dense backward (dK and dV bitwise: same tiles, same
+order; dQ to float32 rounding, as the dense causal dQ pass at d = 128 sums
+the keys of half its query tiles from the diagonal down), a diagonal mask is the dense backward of each diagonal chunk, and queries
 (keys) that see nothing get zero dQ (dK, dV)."""
 
 import math
@@ -85,7 +86,12 @@ def test_sparse_bwd_all_ones_is_dense(dev, d, causal):
     none = fa.fa_bwd_blocksparse(x["q"], x["k"], x["v"], o, x["do"], lse,
                                  None, scale=scale, causal=causal)
     for a, b, c, name in zip(dense, sp, none, ("dQ", "dK", "dV")):
-        assert torch.equal(a, b), f"all-ones mask {name} differs from dense"
+        if name == "dQ" and causal and d == 128:
+            # Same terms, another summation order: float32 rounding only.
+            err = float((a - b).abs().max())
+            assert err <= 1e-5 * float(a.abs().max()), (name, err)
+        else:
+            assert torch.equal(a, b), f"all-ones mask {name} differs from dense"
         assert torch.equal(a, c), f"mask=None {name} differs from dense"
 
 
