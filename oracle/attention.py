@@ -23,7 +23,11 @@ Readings of points the pages leave open:
     scores, LSE_i = m_i + ln(l_i); the pages save the pair (m, l)
     ([TLDR] backward section, [XYZ] key ideas, [Q67] section 5).
   * Causal means key j is visible to query i iff j <= i (equal lengths,
-    top-left aligned); [REAPER] only states the block rule j <= i.
+    top-left aligned); [REAPER] only states the block rule j <= i.  When
+    there are fewer queries than keys (decoding, [REAPER] 3.6, and likewise
+    a prompt fed in chunks), the Nq queries are the last Nq of the Nk
+    tokens: query row r sits at position q_pos0 + r with q_pos0 = Nk - Nq
+    and sees key j iff j <= q_pos0 + r (the square rule at that position).
   * A block mask M has shape ceil(N/block_m) x ceil(N/block_n); key j is
     visible to query i iff M[i // block_m, j // block_n] != 0, and it combines
     with the causal rule by AND ([XYZ] block-sparse extension).
@@ -108,7 +112,8 @@ def _softmax_rows(S):
 
 
 def attention_fwd_head(q, k, v, scale, causal=False, block_mask=None,
-                       block_m=128, block_n=128, rows=None, row_chunk=1024):
+                       block_m=128, block_n=128, rows=None, row_chunk=1024,
+                       q_pos0=0):
     """O and LSE of one head, optionally for a subset of query rows.
 
     The three steps of standard attention ([Q67] section 1; [REAPER] 3.1):
@@ -116,7 +121,8 @@ def attention_fwd_head(q, k, v, scale, causal=False, block_mask=None,
     with masked scores set to -inf before the softmax, and
       LSE_i = m_i + ln(sum_j exp(S_ij - m_i)) = ln(sum_j exp(S_ij)).
     q: (Nq, d), k: (Nk, d), v: (Nk, dv).  Returns O (len(rows), dv) and
-    LSE (len(rows),), both float64.
+    LSE (len(rows),), both float64.  Under the causal rule query row r sits
+    at position q_pos0 + r of the key sequence (``visible``).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n_q, n_k = q.shape[0], k.shape[0]
@@ -126,8 +132,8 @@ def attention_fwd_head(q, k, v, scale, causal=False, block_mask=None,
     for c0 in range(0, rows.size, row_chunk):
         r = rows[c0:c0 + row_chunk]
         S = scale * (q[r] @ k.T)
-        S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n),
-                     S, NEG_INF)
+        S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                             q_pos0), S, NEG_INF)
         P, m, l = _softmax_rows(S)
         O[c0:c0 + r.size] = P @ v
         with np.errstate(divide="ignore"):
@@ -177,9 +183,11 @@ def _each_head(fn, heads, workers):
 
 
 def attention_fwd(Q, K, V, scale, causal=False, block_mask=None, block_m=128,
-                  block_n=128, heads=None, row_chunk=1024, workers=1):
-    """Batched forward over leading dims: Q, K, V of shape (..., N, d); each
-    head is ``attention_fwd_head`` of that head's slices.
+                  block_n=128, heads=None, row_chunk=1024, workers=1,
+                  q_pos0=0):
+    """Batched forward over leading dims: Q (..., Nq, d), K and V
+    (..., Nk, d); each head is ``attention_fwd_head`` of that head's slices
+    (``q_pos0`` as there).
 
     ``heads`` optionally restricts the work to a list of leading-index tuples
     (the other heads of the returned arrays stay NaN); ``workers`` > 1 runs
@@ -194,7 +202,7 @@ def attention_fwd(Q, K, V, scale, causal=False, block_mask=None, block_m=128,
     def one(idx):
         return attention_fwd_head(Q[idx], K[idx], V[idx], scale, causal,
                                   block_mask, block_m, block_n,
-                                  row_chunk=row_chunk)
+                                  row_chunk=row_chunk, q_pos0=q_pos0)
     for idx, (o, lse) in zip(idxs, _each_head(one, idxs, workers)):
         O[idx], LSE[idx] = o, lse
     return O, LSE
@@ -205,7 +213,7 @@ def attention_fwd(Q, K, V, scale, causal=False, block_mask=None, block_m=128,
 # ---------------------------------------------------------------------------
 
 def attention_bwd_head(q, k, v, do, scale, causal=False, block_mask=None,
-                       block_m=128, block_n=128, row_chunk=1024):
+                       block_m=128, block_n=128, row_chunk=1024, q_pos0=0):
     """dQ, dK, dV of one head for the loss L = sum(O * dO).
 
     The pages only say that S and P are rebuilt from saved row statistics
@@ -215,7 +223,8 @@ def attention_bwd_head(q, k, v, do, scale, causal=False, block_mask=None,
       dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij,
       dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
     Masked entries have P = 0 and contribute nothing.  P is recomputed here
-    from its definition, row chunk by row chunk.
+    from its definition, row chunk by row chunk.  q, do: (Nq, .); k, v:
+    (Nk, .); ``q_pos0`` as in ``attention_fwd_head``.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     n_q, n_k = q.shape[0], k.shape[0]
@@ -225,8 +234,8 @@ def attention_bwd_head(q, k, v, do, scale, causal=False, block_mask=None,
     for r0 in range(0, n_q, row_chunk):
         r = np.arange(r0, min(n_q, r0 + row_chunk))
         S = scale * (q[r] @ k.T)
-        S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n),
-                     S, NEG_INF)
+        S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                             q_pos0), S, NEG_INF)
         P, _, _ = _softmax_rows(S)
         dv += P.T @ do[r]
         dP = do[r] @ v.T
@@ -238,7 +247,7 @@ def attention_bwd_head(q, k, v, do, scale, causal=False, block_mask=None,
 
 
 def attention_bwd_rows(q, k, v, do, scale, rows, causal=False,
-                       block_mask=None, block_m=128, block_n=128):
+                       block_mask=None, block_m=128, block_n=128, q_pos0=0):
     """The backward restricted to a set of query rows, for heads too long to
     materialise: dQ of those rows, and their contributions to dK and dV.
 
@@ -248,14 +257,15 @@ def attention_bwd_rows(q, k, v, do, scale, rows, causal=False,
     q[rows] and dv_part = P[rows]^T dO[rows] are the contributions of those
     rows only (under the causal rule, the contributions of rows [N-T, N)
     are the whole dK, dV of keys [N-T, N), which no earlier row sees).
-    Work and memory are O(len(rows) * N * d).
+    Work and memory are O(len(rows) * N * d).  ``q_pos0`` as in
+    ``attention_fwd_head``.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     r = np.asarray(rows, dtype=np.int64)
     n_k = k.shape[0]
     S = scale * (q[r] @ k.T)
-    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n), S,
-                 NEG_INF)
+    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                         q_pos0), S, NEG_INF)
     P, _, _ = _softmax_rows(S)
     dP = do[r] @ v.T
     D = (P * dP).sum(axis=1)
@@ -268,10 +278,10 @@ def attention_bwd_rows(q, k, v, do, scale, rows, causal=False,
 
 def attention_bwd(Q, K, V, dO, scale, causal=False, block_mask=None,
                   block_m=128, block_n=128, heads=None, row_chunk=1024,
-                  workers=1):
+                  workers=1, q_pos0=0):
     """Batched backward over leading dims: each head is
-    ``attention_bwd_head`` of that head's slices (``heads`` and ``workers``
-    as in ``attention_fwd``)."""
+    ``attention_bwd_head`` of that head's slices (``heads``, ``workers`` and
+    ``q_pos0`` as in ``attention_fwd``)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     lead = Q.shape[:-2]
     dQ = np.full(Q.shape, np.nan)
@@ -282,7 +292,7 @@ def attention_bwd(Q, K, V, dO, scale, causal=False, block_mask=None,
     def one(idx):
         return attention_bwd_head(Q[idx], K[idx], V[idx], dO[idx], scale,
                                   causal, block_mask, block_m, block_n,
-                                  row_chunk=row_chunk)
+                                  row_chunk=row_chunk, q_pos0=q_pos0)
     for idx, (dq, dk, dv) in zip(idxs, _each_head(one, idxs, workers)):
         dQ[idx], dK[idx], dV[idx] = dq, dk, dv
     return dQ, dK, dV

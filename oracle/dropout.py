@@ -116,17 +116,23 @@ def dropout_keep(bh, n_q, n_k, seed, t):
     return dropout_bytes(bh, np.arange(n_q), np.arange(n_k), seed) >= t
 
 
-def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None):
+def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None,
+                               block_mask=None, block_m=128, block_n=128,
+                               q_pos0=0):
     """O and LSE of one head with dropout on P (module docstring):
       S = scale Q K^T (masked entries -inf),  P = softmax(S),
       O = (Z * P * 256 / (256 - t)) V,  LSE_i = ln(sum_j exp(S_ij)).
     Returns O (n_q, dv) and LSE (n_q,), float64; with ``rows`` only those
-    query rows (each row of O depends on its own row of S alone)."""
+    query rows (each row of O depends on its own row of S alone).  The
+    visible set is that of ``attention.visible`` (causal rule at position
+    q_pos0 + row, block mask); Z is indexed by the query's row in q and the
+    key's column in k, whatever q_pos0 is."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     n_q, n_k = q.shape[0], k.shape[0]
     r = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
     S = scale * (q[r] @ k.T)
-    S = np.where(visible(r, n_k, causal), S, NEG_INF)
+    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                         q_pos0), S, NEG_INF)
     P, m, l = _softmax_rows(S)
     Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
     Pd = np.where(Z, P, 0.0) * (256.0 / (256.0 - t))
@@ -136,14 +142,18 @@ def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None):
     return O, LSE
 
 
-def attention_bwd_dropout_head(q, k, v, do, scale, causal, t, seed, bh):
+def attention_bwd_dropout_head(q, k, v, do, scale, causal, t, seed, bh,
+                               block_mask=None, block_m=128, block_n=128,
+                               q_pos0=0):
     """dQ, dK, dV of one head with dropout on P, for L = sum(O * dO) with the
-    mask Z fixed (chain rule in the module docstring)."""
+    mask Z fixed (chain rule in the module docstring); visible set and Z as
+    in ``attention_fwd_dropout_head``."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     n_q, n_k = q.shape[0], k.shape[0]
     r = np.arange(n_q)
     S = scale * (q @ k.T)
-    S = np.where(visible(r, n_k, causal), S, NEG_INF)
+    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                         q_pos0), S, NEG_INF)
     P, _, _ = _softmax_rows(S)
     Z = dropout_keep(bh, n_q, n_k, seed, t)
     c = 256.0 / (256.0 - t)
@@ -158,7 +168,9 @@ def attention_bwd_dropout_head(q, k, v, do, scale, causal, t, seed, bh):
     return dq, dk, dv
 
 
-def attention_dq_dropout_rows(q, k, v, do, scale, causal, t, seed, bh, rows):
+def attention_dq_dropout_rows(q, k, v, do, scale, causal, t, seed, bh, rows,
+                              block_mask=None, block_m=128, block_n=128,
+                              q_pos0=0):
     """dQ of the given query rows of one head with dropout on P: row i of dQ
     needs only row i of P, dP and D (same chain rule as
     ``attention_bwd_dropout_head``), so heads too long to materialise can be
@@ -167,7 +179,8 @@ def attention_dq_dropout_rows(q, k, v, do, scale, causal, t, seed, bh, rows):
     n_k = k.shape[0]
     r = np.asarray(rows, dtype=np.int64)
     S = scale * (q[r] @ k.T)
-    S = np.where(visible(r, n_k, causal), S, NEG_INF)
+    S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
+                         q_pos0), S, NEG_INF)
     P, _, _ = _softmax_rows(S)
     Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
     c = 256.0 / (256.0 - t)

@@ -571,6 +571,87 @@ def check_batched_wrappers(orc):
         _close(t, a, 1e-13, "threaded gradients")
 
 
+def check_offset_queries(orc):
+    """Fewer queries than keys, the queries being the last Nq tokens
+    (q_pos0 = Nk - Nq; decoding and prompts fed in chunks, [REAPER] 3.6):
+    forward and backward against PyTorch's float64 attention and autograd
+    under the explicit element mask (the causal rule at position q_pos0 + r
+    AND a block mask of ceil(Nq/bm) x ceil(Nk/bn) entries, built here with
+    Python loops), including rows that see no key; the causal forward equals
+    ``attention_decode_head``; the causal backward equals that of the square
+    problem over all Nk tokens whose first Nk - Nq query rows carry dO = 0
+    (such rows contribute nothing to dK and dV); the row-restricted backward
+    and the batched wrappers take the same offset."""
+    r = _rng(43)
+    d, dv, bm_, bn_, scale = 4, 3, 2, 3, 0.6
+    for n_q, n_k in ((3, 8), (5, 5), (1, 7), (6, 13)):
+        off = n_k - n_q
+        q, k = r.standard_normal((n_q, d)), r.standard_normal((n_k, d))
+        v, do = r.standard_normal((n_k, dv)), r.standard_normal((n_q, dv))
+        mask = (r.random((-(-n_q // bm_), -(-n_k // bn_))) < 0.6).astype(
+            np.uint8)
+        mask[0, 0] = 1
+        for causal in (False, True):
+            for m in (None, mask):
+                vis = np.array([[(not causal or j <= off + i) and
+                                 (m is None or m[i // bm_][j // bn_] != 0)
+                                 for j in range(n_k)] for i in range(n_q)])
+                live = vis.any(axis=1)
+                e2 = vis.copy()
+                e2[~live] = True
+                To, Tl, Tdq, Tdk, Tdv = _torch_reference(
+                    q, k, v, np.where(live[:, None], do, 0.0), scale, False,
+                    e2)
+                tag = f"offset {n_q}x{n_k} causal={causal} mask={m is not None}"
+                O, lse = orc.attention_fwd_head(q, k, v, scale, causal, m, bm_,
+                                                bn_, q_pos0=off)
+                dq, dk, dv_ = orc.attention_bwd_head(q, k, v, do, scale,
+                                                     causal, m, bm_, bn_,
+                                                     q_pos0=off)
+                _close(O[live], To[live], 1e-12, tag + " O")
+                _close(lse[live], Tl[live], 1e-12, tag + " LSE")
+                assert np.all(O[~live] == 0.0), tag + " empty O"
+                assert np.all(np.isneginf(lse[~live])), tag + " empty LSE"
+                _close(dq[live], Tdq[live], 1e-12, tag + " dQ")
+                assert np.all(dq[~live] == 0.0), tag + " empty dQ"
+                _close(dk, Tdk, 1e-12, tag + " dK")
+                _close(dv_, Tdv, 1e-12, tag + " dV")
+                dq_r, dk_r, dv_r = orc.attention_bwd_rows(
+                    q, k, v, do, scale, np.arange(n_q), causal, m, bm_, bn_,
+                    q_pos0=off)
+                _close(dq_r, dq, 1e-12, tag + " rows dQ")
+                _close(dk_r, dk, 1e-12, tag + " rows dK")
+                _close(dv_r, dv_, 1e-12, tag + " rows dV")
+        O_d, l_d = orc.attention_decode_head(q, k, v, scale, True)
+        O, lse = orc.attention_fwd_head(q, k, v, scale, True, q_pos0=off)
+        _close(O, O_d, EXACT_TOL, "offset forward = decode O")
+        _close(lse, l_d, EXACT_TOL, "offset forward = decode LSE")
+        q_full = np.concatenate([r.standard_normal((off, d)), q])
+        do_full = np.concatenate([np.zeros((off, dv)), do])
+        gq, gk, gv = orc.attention_bwd_head(q_full, k, v, do_full, scale, True)
+        dq, dk, dv_ = orc.attention_bwd_head(q, k, v, do, scale, True,
+                                             q_pos0=off)
+        _close(dq, gq[off:], EXACT_TOL, "offset = padded square dQ")
+        _close(dk, gk, EXACT_TOL, "offset = padded square dK")
+        _close(dv_, gv, EXACT_TOL, "offset = padded square dV")
+    B, H, n_q, n_k = 2, 2, 3, 7
+    Q, dO = r.standard_normal((B, H, n_q, d)), r.standard_normal((B, H, n_q, dv))
+    K, V = r.standard_normal((B, H, n_k, d)), r.standard_normal((B, H, n_k, dv))
+    O, lse = orc.attention_fwd(Q, K, V, scale, True, q_pos0=n_k - n_q)
+    g = orc.attention_bwd(Q, K, V, dO, scale, True, q_pos0=n_k - n_q)
+    for b in range(B):
+        for h in range(H):
+            vis = np.array([[j <= n_k - n_q + i for j in range(n_k)]
+                            for i in range(n_q)])
+            To, Tl, Tdq, Tdk, Tdv = _torch_reference(
+                Q[b, h], K[b, h], V[b, h], dO[b, h], scale, False, vis)
+            tag = f"batched offset ({b},{h})"
+            _close(O[b, h], To, 1e-12, tag + " O")
+            _close(lse[b, h], Tl, 1e-12, tag + " LSE")
+            for a, t, nm in zip(g, (Tdq, Tdk, Tdv), ("dQ", "dK", "dV")):
+                _close(a[b, h], t, 1e-12, f"{tag} {nm}")
+
+
 ALL_CHECKS = [
     check_fig1_divide_last,
     check_fig2_streamed_pairs,
@@ -590,4 +671,5 @@ ALL_CHECKS = [
     check_decode,
     check_bwd_rows,
     check_batched_wrappers,
+    check_offset_queries,
 ]

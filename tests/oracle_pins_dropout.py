@@ -238,6 +238,75 @@ def check_d_identity(drp):
         _close((P * dP).sum(axis=1), (do * O).sum(axis=1), 1e-12, "D identity")
 
 
+def _torch_dropout(q, k, v, do, scale, vis, keep, t):
+    """PyTorch float64 autograd of O = (Z * softmax(S) * 256/(256-t)) V with
+    S = scale Q K^T masked by the element mask ``vis`` (every row has a
+    visible key)."""
+    import torch
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                  for x in (q, k, v))
+    S = (scale * tq @ tk.T).masked_fill(~torch.tensor(vis), float("-inf"))
+    P = torch.softmax(S, dim=1)
+    Pd = P * torch.tensor(keep, dtype=torch.float64) * (256.0 / (256.0 - t))
+    o = Pd @ tv
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    lse = torch.logsumexp(S, dim=1)
+    return (o.detach().numpy(), lse.detach().numpy(), tq.grad.numpy(),
+            tk.grad.numpy(), tv.grad.numpy())
+
+
+def check_block_mask_and_offset(drp):
+    """Dropout with a block mask and with fewer queries than keys (the causal
+    rule at position q_pos0 + r): forward, LSE and gradients against
+    PyTorch's float64 autograd of the definition, with the element mask built
+    here with Python loops and Z taken from the keep function (pinned above
+    against the published Philox values); Z is indexed by the query's row in
+    Q, not by its position.  Rows with no visible key get O = 0, LSE = -inf
+    and dQ = 0; the row-restricted dQ takes the same mask and offset."""
+    r = np.random.default_rng(37)
+    d, bm_, bn_, t, seed, bh = 4, 2, 3, 90, 2024, 3
+    for n_q, n_k in ((5, 9), (7, 7), (2, 6)):
+        off = n_k - n_q
+        q, do = r.standard_normal((n_q, d)), r.standard_normal((n_q, d))
+        k, v = r.standard_normal((n_k, d)), r.standard_normal((n_k, d))
+        mask = (r.random((-(-n_q // bm_), -(-n_k // bn_))) < 0.6).astype(
+            np.uint8)
+        mask[0, 0] = 1
+        mask[-1, :] = 0                       # the last rows see nothing
+        keep = drp.dropout_keep(bh, n_q, n_k, seed, t)
+        for causal in (False, True):
+            vis = np.array([[(not causal or j <= off + i) and
+                             mask[i // bm_][j // bn_] != 0
+                             for j in range(n_k)] for i in range(n_q)])
+            live = vis.any(axis=1)
+            assert not live.all()
+            e2 = vis.copy()
+            e2[~live] = True
+            To, Tl, Tdq, Tdk, Tdv = _torch_dropout(
+                q, k, v, np.where(live[:, None], do, 0.0), 0.7, e2, keep, t)
+            kw = dict(block_mask=mask, block_m=bm_, block_n=bn_, q_pos0=off)
+            O, L = drp.attention_fwd_dropout_head(q, k, v, 0.7, causal, t,
+                                                  seed, bh, **kw)
+            dq, dk, dv = drp.attention_bwd_dropout_head(q, k, v, do, 0.7,
+                                                        causal, t, seed, bh,
+                                                        **kw)
+            tag = f"masked dropout {n_q}x{n_k} causal={causal}"
+            _close(O[live], To[live], 1e-12, tag + " O")
+            _close(L[live], Tl[live], 1e-12, tag + " LSE")
+            assert np.all(O[~live] == 0.0) and np.all(np.isneginf(L[~live]))
+            _close(dq[live], Tdq[live], 1e-12, tag + " dQ")
+            assert np.all(dq[~live] == 0.0), tag + " empty dQ"
+            _close(dk, Tdk, 1e-12, tag + " dK")
+            _close(dv, Tdv, 1e-12, tag + " dV")
+            rows = np.array([0, n_q - 1])
+            dqr = drp.attention_dq_dropout_rows(q, k, v, do, 0.7, causal, t,
+                                                seed, bh, rows, **kw)
+            _close(dqr, dq[rows], 1e-12, tag + " dQ rows")
+            Or, Lr = drp.attention_fwd_dropout_head(q, k, v, 0.7, causal, t,
+                                                    seed, bh, rows=rows, **kw)
+            _close(Or, O[rows], 1e-13, tag + " forward rows")
+
+
 ALL_CHECKS = [
     check_philox_kat,
     check_mask_layout,
@@ -249,4 +318,5 @@ ALL_CHECKS = [
     check_brute_force_python,
     check_row_subsets,
     check_d_identity,
+    check_block_mask_and_offset,
 ]

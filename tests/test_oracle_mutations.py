@@ -98,6 +98,18 @@ MUTATIONS = [
     ("batched bwd: causal rule dropped",
      "dO[idx], scale,\n                                  causal,",
      "dO[idx], scale,\n                                  False,", 0),
+    ("offset fwd: query offset ignored", "q_pos0), S, NEG_INF)",
+     "0), S, NEG_INF)", 0),
+    ("offset bwd: query offset ignored", "q_pos0), S, NEG_INF)",
+     "0), S, NEG_INF)", 1),
+    ("offset bwd rows: query offset ignored", "q_pos0), S, NEG_INF)",
+     "0), S, NEG_INF)", 2),
+    ("offset bwd: offset counted from the wrong end", "q_pos0), S, NEG_INF)",
+     "-q_pos0), S, NEG_INF)", 1),
+    ("batched fwd: offset not passed", "row_chunk=row_chunk, q_pos0=q_pos0)",
+     "row_chunk=row_chunk)", 0),
+    ("batched bwd: offset not passed", "row_chunk=row_chunk, q_pos0=q_pos0)",
+     "row_chunk=row_chunk)", 1),
 ]
 
 
@@ -167,6 +179,15 @@ DROPOUT_MUTATIONS = [
      "dS = P * dP\n    return", 0),
     ("fwd rows: mask of the first rows", "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t",
      "Z = dropout_bytes(bh, np.arange(len(r)), np.arange(n_k), seed) >= t", 0),
+    ("fwd: key blocks collapsed", "block_n,\n                         q_pos0), S, NEG_INF)",
+     "block_n * 0 + 10**6,\n                         q_pos0), S, NEG_INF)", 0),
+    ("bwd: block sizes swapped",
+     "causal, block_mask, block_m, block_n,\n                         q_pos0), S, NEG_INF)",
+     "causal, block_mask, block_n, block_m,\n                         q_pos0), S, NEG_INF)", 1),
+    ("bwd: query offset ignored", "q_pos0), S, NEG_INF)", "0), S, NEG_INF)", 1),
+    ("dq rows: query offset ignored", "q_pos0), S, NEG_INF)", "0), S, NEG_INF)", 2),
+    ("fwd: Z indexed by position", "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t\n    Pd",
+     "Z = dropout_bytes(bh, r + q_pos0, np.arange(n_k), seed) >= t\n    Pd", 0),
 ]
 
 
