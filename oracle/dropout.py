@@ -19,11 +19,14 @@ here:
     (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1,
     2, 3", SC 2011): one call maps a 128-bit counter and a 64-bit key to
     four 32-bit words.  Element (bh, i, j) of head bh (batch-major flattened
-    index b*H + h), query row i and key column j uses the call with counter
-    (i >> 2, j >> 2, bh, 0) and key (seed mod 2^32, seed >> 32); word
-    (i & 3) of its output, byte (j & 3) of that word (bits 8(j&3) ..
-    8(j&3)+7) is the element's random byte u.  So one call covers a 4 x 4
-    block of the score matrix, and the mask does not depend on any tiling.
+    index b*H + h), query row i (the row of Q) and key column j uses the call
+    with counter (i >> 2, j >> 2, bh, q_pos0) and key (seed mod 2^32,
+    seed >> 32); word (i & 3) of its output, byte (j & 3) of that word (bits
+    8(j&3) .. 8(j&3)+7) is the element's random byte u.  So one call covers a
+    4 x 4 block of the score matrix, and the mask does not depend on any
+    tiling.  q_pos0 is the position of query row 0 in the key sequence (0
+    when queries and keys are the same tokens): queries fed in chunks at
+    different offsets draw from disjoint counters.
   * The drop probability is quantised to t / 256 with t = round(256 p), an
     integer in [0, 255]: the element is kept iff u >= t, and survivors are
     scaled by 256 / (256 - t).
@@ -93,7 +96,7 @@ def dropout_threshold(p):
     return t
 
 
-def dropout_bytes(bh, rows, cols, seed):
+def dropout_bytes(bh, rows, cols, seed, q_pos0=0):
     """The random byte u of every element (bh, i, j), i in rows, j in cols
     (uint8 array of shape (len(rows), len(cols))), following the element to
     counter mapping stated in the module docstring."""
@@ -102,7 +105,8 @@ def dropout_bytes(bh, rows, cols, seed):
     rb = np.unique(rows >> 2)
     cb = np.unique(cols >> 2)
     R, C = np.meshgrid(rb, cb, indexing="ij")
-    ctr = np.stack([R, C, np.full_like(R, bh), np.zeros_like(R)], axis=-1)
+    ctr = np.stack([R, C, np.full_like(R, bh), np.full_like(R, q_pos0)],
+                   axis=-1)
     words = philox4x32_10(ctr, (seed & _MASK32, (seed >> 32) & _MASK32))
     ri = np.searchsorted(rb, rows >> 2)
     ci = np.searchsorted(cb, cols >> 2)
@@ -111,9 +115,10 @@ def dropout_bytes(bh, rows, cols, seed):
     return ((w >> shift) & 0xFF).astype(np.uint8)
 
 
-def dropout_keep(bh, n_q, n_k, seed, t):
+def dropout_keep(bh, n_q, n_k, seed, t, q_pos0=0):
     """Boolean keep mask Z (n_q, n_k) of head bh: u >= t."""
-    return dropout_bytes(bh, np.arange(n_q), np.arange(n_k), seed) >= t
+    return dropout_bytes(bh, np.arange(n_q), np.arange(n_k), seed,
+                         q_pos0) >= t
 
 
 def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None,
@@ -125,8 +130,8 @@ def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None,
     Returns O (n_q, dv) and LSE (n_q,), float64; with ``rows`` only those
     query rows (each row of O depends on its own row of S alone).  The
     visible set is that of ``attention.visible`` (causal rule at position
-    q_pos0 + row, block mask); Z is indexed by the query's row in q and the
-    key's column in k, whatever q_pos0 is."""
+    q_pos0 + row, block mask); Z is that of ``dropout_bytes`` with the same
+    q_pos0."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     n_q, n_k = q.shape[0], k.shape[0]
     r = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -134,7 +139,7 @@ def attention_fwd_dropout_head(q, k, v, scale, causal, t, seed, bh, rows=None,
     S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
                          q_pos0), S, NEG_INF)
     P, m, l = _softmax_rows(S)
-    Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
+    Z = dropout_bytes(bh, r, np.arange(n_k), seed, q_pos0) >= t
     Pd = np.where(Z, P, 0.0) * (256.0 / (256.0 - t))
     O = Pd @ v
     with np.errstate(divide="ignore"):
@@ -155,7 +160,7 @@ def attention_bwd_dropout_head(q, k, v, do, scale, causal, t, seed, bh,
     S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
                          q_pos0), S, NEG_INF)
     P, _, _ = _softmax_rows(S)
-    Z = dropout_keep(bh, n_q, n_k, seed, t)
+    Z = dropout_keep(bh, n_q, n_k, seed, t, q_pos0)
     c = 256.0 / (256.0 - t)
     Pd = np.where(Z, P, 0.0) * c
     dv = Pd.T @ do
@@ -182,7 +187,7 @@ def attention_dq_dropout_rows(q, k, v, do, scale, causal, t, seed, bh, rows,
     S = np.where(visible(r, n_k, causal, block_mask, block_m, block_n,
                          q_pos0), S, NEG_INF)
     P, _, _ = _softmax_rows(S)
-    Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t
+    Z = dropout_bytes(bh, r, np.arange(n_k), seed, q_pos0) >= t
     c = 256.0 / (256.0 - t)
     dP = np.where(Z, do[r] @ v.T, 0.0) * c
     D = (P * dP).sum(axis=1)

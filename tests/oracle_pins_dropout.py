@@ -67,20 +67,21 @@ def _philox_py(ctr, key):
 
 def check_mask_layout(drp):
     """Element (bh, i, j) takes byte (j & 3) of word (i & 3) of the call with
-    counter (i >> 2, j >> 2, bh, 0) and key (seed low, seed high)."""
+    counter (i >> 2, j >> 2, bh, q_pos0) and key (seed low, seed high)."""
     seed = 0x0123456789ABCDEF
     rows = [0, 1, 2, 3, 5, 6, 17, 130, 1023, 4097]
     cols = [0, 1, 2, 3, 4, 7, 9, 255, 1000, 8191]
-    for bh in (0, 3, 63):
-        got = drp.dropout_bytes(bh, rows, cols, seed)
+    for bh, off in ((0, 0), (3, 0), (63, 0), (3, 5), (1, 4096)):
+        got = (drp.dropout_bytes(bh, rows, cols, seed) if off == 0 else
+               drp.dropout_bytes(bh, rows, cols, seed, off))
         for a, i in enumerate(rows):
             for b, j in enumerate(cols):
-                w = _philox_py((i >> 2, j >> 2, bh, 0),
+                w = _philox_py((i >> 2, j >> 2, bh, off),
                                (seed & 0xFFFFFFFF, seed >> 32))[i & 3]
                 want = (w >> (8 * (j & 3))) & 0xFF
                 assert int(got[a, b]) == want, (
-                    f"byte of (bh={bh}, i={i}, j={j}): {int(got[a, b])} "
-                    f"!= {want}")
+                    f"byte of (bh={bh}, i={i}, j={j}, q_pos0={off}): "
+                    f"{int(got[a, b])} != {want}")
 
 
 def check_keep_fraction(drp):
@@ -259,10 +260,10 @@ def check_block_mask_and_offset(drp):
     """Dropout with a block mask and with fewer queries than keys (the causal
     rule at position q_pos0 + r): forward, LSE and gradients against
     PyTorch's float64 autograd of the definition, with the element mask built
-    here with Python loops and Z taken from the keep function (pinned above
-    against the published Philox values); Z is indexed by the query's row in
-    Q, not by its position.  Rows with no visible key get O = 0, LSE = -inf
-    and dQ = 0; the row-restricted dQ takes the same mask and offset."""
+    here with Python loops and Z taken from the keep function at the same
+    offset (its layout pinned above element by element).  Rows with no
+    visible key get O = 0, LSE = -inf and dQ = 0; the row-restricted dQ
+    takes the same mask and offset."""
     r = np.random.default_rng(37)
     d, bm_, bn_, t, seed, bh = 4, 2, 3, 90, 2024, 3
     for n_q, n_k in ((5, 9), (7, 7), (2, 6)):
@@ -273,7 +274,7 @@ def check_block_mask_and_offset(drp):
             np.uint8)
         mask[0, 0] = 1
         mask[-1, :] = 0                       # the last rows see nothing
-        keep = drp.dropout_keep(bh, n_q, n_k, seed, t)
+        keep = drp.dropout_keep(bh, n_q, n_k, seed, t, off)
         for causal in (False, True):
             vis = np.array([[(not causal or j <= off + i) and
                              mask[i // bm_][j // bn_] != 0

@@ -160,7 +160,7 @@ DROPOUT_MUTATIONS = [
     ("mapping: seed halves swapped",
      "(seed & _MASK32, (seed >> 32) & _MASK32)",
      "((seed >> 32) & _MASK32, seed & _MASK32)", 0),
-    ("keep: strict comparison", "seed) >= t", "seed) > t", 0),
+    ("keep: strict comparison", "q_pos0) >= t\n\n\ndef attention_fwd", "q_pos0) > t\n\n\ndef attention_fwd", 0),
     ("threshold: truncated", "t = int(np.rint(256.0 * float(p)))",
      "t = int(256.0 * float(p))", 0),
     ("fwd: survivors not rescaled", "Pd = np.where(Z, P, 0.0) * (256.0 / (256.0 - t))",
@@ -177,8 +177,8 @@ DROPOUT_MUTATIONS = [
      "dP = np.where(Z, do[r] @ v.T, 0.0)", 0),
     ("dq rows: D term dropped", "dS = P * (dP - D[:, None])\n    return",
      "dS = P * dP\n    return", 0),
-    ("fwd rows: mask of the first rows", "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t",
-     "Z = dropout_bytes(bh, np.arange(len(r)), np.arange(n_k), seed) >= t", 0),
+    ("fwd rows: mask of the first rows", "Z = dropout_bytes(bh, r, np.arange(n_k), seed, q_pos0) >= t",
+     "Z = dropout_bytes(bh, np.arange(len(r)), np.arange(n_k), seed, q_pos0) >= t", 0),
     ("fwd: key blocks collapsed", "block_n,\n                         q_pos0), S, NEG_INF)",
      "block_n * 0 + 10**6,\n                         q_pos0), S, NEG_INF)", 0),
     ("bwd: block sizes swapped",
@@ -186,8 +186,13 @@ DROPOUT_MUTATIONS = [
      "causal, block_mask, block_n, block_m,\n                         q_pos0), S, NEG_INF)", 1),
     ("bwd: query offset ignored", "q_pos0), S, NEG_INF)", "0), S, NEG_INF)", 1),
     ("dq rows: query offset ignored", "q_pos0), S, NEG_INF)", "0), S, NEG_INF)", 2),
-    ("fwd: Z indexed by position", "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t\n    Pd",
-     "Z = dropout_bytes(bh, r + q_pos0, np.arange(n_k), seed) >= t\n    Pd", 0),
+    ("fwd: Z indexed by position", "Z = dropout_bytes(bh, r, np.arange(n_k), seed, q_pos0) >= t\n    Pd",
+     "Z = dropout_bytes(bh, r + q_pos0, np.arange(n_k), seed, q_pos0) >= t\n    Pd", 0),
+    ("fwd: Z without the offset", "Z = dropout_bytes(bh, r, np.arange(n_k), seed, q_pos0) >= t\n    Pd",
+     "Z = dropout_bytes(bh, r, np.arange(n_k), seed) >= t\n    Pd", 0),
+    ("bwd: Z without the offset", "Z = dropout_keep(bh, n_q, n_k, seed, t, q_pos0)",
+     "Z = dropout_keep(bh, n_q, n_k, seed, t)", 0),
+    ("mapping: offset not in the counter", "np.full_like(R, q_pos0)],", "np.zeros_like(R)],", 0),
 ]
 
 
