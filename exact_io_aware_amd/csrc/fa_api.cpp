@@ -43,6 +43,21 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dt,
   return FA_OK;
 }
 
+// The key length of a call whose keys may differ from its queries (Nq =
+// the N checked above): 1 <= Nk <= 2^30 when there are queries, the same
+// offset and grid limits on the key side, and Nq <= Nk under the causal rule
+// (the queries are the last Nq of the Nk tokens).
+fa_status check_keys(int64_t bh, int64_t Nq, int64_t Nk, int64_t d,
+                     int causal) {
+  if (Nk < 0) return FA_ERR_SHAPE;
+  if (bh == 0) return FA_OK;  // nothing to compute (B, H or Nq is 0)
+  if (Nk == 0 || Nk > kMaxN) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (bh > ((int64_t)1 << 62) / (Nk * d)) return FA_ERR_SHAPE;
+  if (bh * ((Nk + 63) / 64) > (int64_t)0x7fffffff) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
 size_t ws_rows(int64_t bh, int64_t n) {
@@ -70,10 +85,13 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
                      int64_t block_m, int64_t block_n, bool sparse_call,
                      void* stream, int drop_t = 0, uint64_t seed = 0,
                      bool count_call = false, int32_t* visits = nullptr,
-                     size_t visits_len = 0) {
+                     size_t visits_len = 0, int64_t Nk = -1) {
   bool empty = false;
   int64_t bh = 0;
   fa_status st = check_shape(B, H, N, d, dt, &empty, &bh);
+  if (st != FA_OK) return st;
+  if (Nk < 0) Nk = N;  // keys and queries are the same tokens
+  st = check_keys(bh, N, Nk, d, causal);
   if (st != FA_OK) return st;
   if (!scale_ok(scale)) return FA_ERR_ARG;
   if (sparse_call) {
@@ -104,13 +122,15 @@ fa_status fwd_common(const void* q, const void* k, const void* v, void* o,
   a.lse = lse;
   a.bh = bh;
   a.n = (int)N;
+  a.nk = (int)Nk;
+  a.q_off = (int)(Nk - N);
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
   a.mask = sparse_call ? mask : nullptr;
   a.block_m = (int)(sparse_call ? block_m : 128);
   a.block_n = (int)(sparse_call ? block_n : 128);
-  a.mask_cols = (int)((N + a.block_n - 1) / a.block_n);
+  a.mask_cols = (int)((Nk + a.block_n - 1) / a.block_n);
   a.drop_t = drop_t;
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
@@ -135,9 +155,12 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
                      bool check_scale, int causal, fa::BwdArgs* out,
                      bool* empty, const uint8_t* mask = nullptr,
                      int64_t block_m = 128, int64_t block_n = 128,
-                     bool sparse_call = false) {
+                     bool sparse_call = false, int64_t Nk = -1) {
   int64_t bh = 0;
   fa_status st = check_shape(B, H, N, d, dt, empty, &bh);
+  if (st != FA_OK) return st;
+  if (Nk < 0) Nk = N;  // keys and queries are the same tokens
+  st = check_keys(bh, N, Nk, d, causal);
   if (st != FA_OK) return st;
   if (check_scale && !scale_ok(scale)) return FA_ERR_ARG;
   if (sparse_call) {
@@ -172,13 +195,15 @@ fa_status bwd_common(unsigned need, const void* q, const void* k,
   a.ws_lse2 = ws + ws_rows(bh, N);
   a.bh = bh;
   a.n = (int)N;
+  a.nk = (int)Nk;
+  a.q_off = (int)(Nk - N);
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
   a.mask = sparse_call ? mask : nullptr;
   a.block_m = (int)(sparse_call ? block_m : 128);
   a.block_n = (int)(sparse_call ? block_n : 128);
-  a.mask_cols = (int)((N + a.block_n - 1) / a.block_n);
+  a.mask_cols = (int)((Nk + a.block_n - 1) / a.block_n);
   *out = a;
   return FA_OK;
 }
@@ -480,6 +505,58 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                             true, causal, &a, &empty, mask, block_m, block_n,
                             true);
   if (st != FA_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(run_pre(a, dt, s));
+  if (st != FA_OK) return st;
+  st = from_hip(run_dkdv(a, dt, s));
+  if (st != FA_OK) return st;
+  return from_hip(run_dq(a, dt, s));
+}
+
+fa_status fa_fwd_general(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t Nq,
+                         int64_t Nk, int64_t d, fa_dtype dt, float scale,
+                         int causal, const uint8_t* mask, int64_t block_m,
+                         int64_t block_n, float p_drop, uint64_t seed,
+                         void* stream) {
+  if (Nk < 0) return FA_ERR_SHAPE;  // (fwd_common reads Nk < 0 as Nk = Nq)
+  bool empty = false;
+  int64_t bh = 0;
+  fa_status st = check_shape(B, H, Nq, d, dt, &empty, &bh);
+  if (st != FA_OK) return st;
+  st = check_keys(bh, Nq, Nk, d, causal);
+  if (st != FA_OK) return st;
+  int t = 0;
+  if (!scale_ok(scale) || !dropout_t(p_drop, &t)) return FA_ERR_ARG;
+  if (t > 0 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  return fwd_common(q, k, v, o, lse, B, H, Nq, d, dt, scale, causal, mask,
+                    block_m, block_n, mask != nullptr, stream, t, seed, false,
+                    nullptr, 0, Nk);
+}
+
+fa_status fa_bwd_general(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, fa_dtype dt,
+                         float scale, int causal, const uint8_t* mask,
+                         int64_t block_m, int64_t block_n, float p_drop,
+                         uint64_t seed, void* stream) {
+  if (Nk < 0) return FA_ERR_SHAPE;  // (bwd_common reads Nk < 0 as Nk = Nq)
+  fa::BwdArgs a{};
+  bool empty = false;
+  fa_status st = bwd_common(0x1ffu, q, k, v, o, dout, lse, dq, dk, dv,
+                            workspace, workspace_bytes, B, H, Nq, d, dt, scale,
+                            true, causal, &a, &empty, mask, block_m, block_n,
+                            mask != nullptr, Nk);
+  if (st != FA_OK) return st;
+  int t = 0;
+  if (!dropout_t(p_drop, &t)) return FA_ERR_ARG;
+  if (t > 0 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  a.drop_t = t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = from_hip(run_pre(a, dt, s));
   if (st != FA_OK) return st;

@@ -144,8 +144,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ ws_d,
                      const float* __restrict__ ws_lse2, float* __restrict__ dK,
-                     float* __restrict__ dV, int n, int n_ktiles, int total,
-                     int bundle, float c_log2, float scale,
+                     float* __restrict__ dV, int n, int nk, int q_off,
+                     int n_ktiles, int total, int bundle, float c_log2,
+                     float scale,
                      const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n, Dropout drop,
                      int* __restrict__ visits) {
@@ -179,7 +180,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     head = pl.head;
     kt_a = pl.rank;
   }
-  const int64_t hoff = (int64_t)head * n * D;
+  const int64_t hoff = (int64_t)head * n * D;     // Q, dO: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V, dK, dV: nk rows
   const int64_t roff = (int64_t)head * n;
   drop.bh = (uint32_t)head;
 
@@ -189,16 +191,17 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int kw0 = k0 + 32 * kw;
   const int key = kw0 + l32;
 
-  // K and V tiles of the workgroup (rows past the end read row n - 1; their
-  // dK, dV are never stored).
+  // K and V tiles of the workgroup (rows past the end read row nk - 1;
+  // their dK, dV are never stored).
 #pragma unroll
   for (int i = 0; i < T::KV_BLK; ++i) {
-    dma_tile_block<D>(K + hoff, k0, n, smem, w + T::NW * i, lane);
-    dma_tile_block<D>(V + hoff, k0, n, smem + T::OFF_V, w + T::NW * i, lane);
+    dma_tile_block<D>(K + hoff_k, k0, nk, smem, w + T::NW * i, lane);
+    dma_tile_block<D>(V + hoff_k, k0, nk, smem + T::OFF_V, w + T::NW * i, lane);
   }
 
   const int n_qt = (n + T::BRQ - 1) / T::BRQ;
-  const int qt_begin = CAUSAL ? k0 / T::BRQ : 0;
+  // Under the causal rule query row i sees key k0 from i = k0 - q_off on.
+  const int qt_begin = CAUSAL ? max(0, k0 - q_off) / T::BRQ : 0;
   // DMA sources of the Q / dO tiles: lane `lane` fills bytes 16*lane of
   // 1-KB block w + NW*i, i.e. row o / ROW, physical chunk (o % ROW) / 16 =
   // logical chunk ^ swizzle; element offsets from the tile's first row.
@@ -311,7 +314,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int qi = 0; qi < T::QBW; ++qi) {
       const int qb = qh * T::QBW + qi;
       const int qq0 = qt * T::BRQ + qb * 32;
-      if (MASK && CAUSAL && qq0 + 31 < kw0) continue;  // every query before every key
+      if (MASK && CAUSAL && qq0 + 31 + q_off < kw0) continue;  // every query before every key
       // Dropout: dV takes the kept probabilities (the 1/(1-p) factor is
       // applied at the end), dS the kept and rescaled dP.
       uint32_t u[4];
@@ -329,7 +332,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.  With MASK, P is
       // zero for queries before this lane's key or past the end: qrel is the
       // first visible query relative to qq0 + h*4, qend the end.
-      const int qlo = (CAUSAL ? key : 0) - qq0 - h * 4;
+      const int qlo = (CAUSAL ? key - q_off : 0) - qq0 - h * 4;
       const int qhi = n - qq0 - h * 4;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -394,11 +397,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   } else if (qt_begin < n_qt) {
     issue_stage(qt_begin, 0);
-    // Masked tiles: under the causal rule those holding the first 128
-    // queries (they meet the diagonal of the workgroup's keys), and the
-    // tile reaching past the end.  Unmasked tiles run in pairs with static
-    // stage parity (stage = (qt - qt_begin) & 1).
-    const int head_end = min(n_qt, qt_begin + (CAUSAL ? T::BCK / T::BRQ : 0));
+    // Masked tiles: under the causal rule those holding a query that does
+    // not see the workgroup's last key k0 + 127 (query + q_off < k0 + 127:
+    // they meet the diagonal), and the tile reaching past the end.
+    // Unmasked tiles run in pairs with static stage parity (stage =
+    // (qt - qt_begin) & 1).
+    const int diag_last = k0 + T::BCK - 2 - q_off;  // last such query
+    const int head_end =
+        (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
     const int full_end = n / T::BRQ;  // tiles before this are fully in range
     int qt = qt_begin;
 #pragma unroll 1
@@ -442,9 +448,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   }
   __syncthreads();
-  if (qh == 0 && key < n) {
-    float* dkr = dK + hoff + (int64_t)key * D;
-    float* dvr = dV + hoff + (int64_t)key * D;
+  if (qh == 0 && key < nk) {
+    float* dkr = dK + hoff_k + (int64_t)key * D;
+    float* dvr = dV + hoff_k + (int64_t)key * D;
     // D layout of dK^T / dV^T: lane = key, register i -> d = db*32 + (i/4)*8 + h*4 + i%4.
 #pragma unroll
     for (int db = 0; db < T::DB; ++db) {
@@ -506,8 +512,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ ws_d,
                    const float* __restrict__ ws_lse2, float* __restrict__ dQ,
-                   int n, int n_qtiles, int total, int bundle, float c_log2,
-                   float scale,
+                   int n, int nk, int q_off, int n_qtiles, int total,
+                   int bundle, float c_log2, float scale,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
                    int block_n, Dropout drop, int* __restrict__ visits) {
   using T = QTile<D, NW>;
@@ -536,9 +542,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     head = pl.head;
     qt_a = CAUSAL ? (n_qtiles - 1 - pl.rank) : pl.rank;
   }
-  const int64_t hoff = (int64_t)head * n * D;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
+  const int64_t hoff = (int64_t)head * n * D;     // Q, dO, dQ: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V: nk rows
+  const bf16* Kh = K + hoff_k;
+  const bf16* Vh = V + hoff_k;
   drop.bh = (uint32_t)head;
 
   // One query tile of 32 * NW rows; REV walks its key tiles from the
@@ -582,7 +589,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int kb0 = kt * T::BCK;
     const bf16* kbase = Kh + (int64_t)kb0 * D;
     const bf16* vbase = Vh + (int64_t)kb0 * D;
-    if (kb0 + T::BCK <= n) {
+    if (kb0 + T::BCK <= nk) {
 #pragma unroll
       for (int i = 0; i < T::BLK; ++i) {
         dma16(kbase + (uint32_t)goff[i], st + (w + NW * i) * 1024);
@@ -591,19 +598,20 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     } else {
 #pragma unroll
       for (int i = 0; i < T::BLK; ++i) {
-        dma_tile_block<D>(Kh, kb0, n, st, w + NW * i, lane);
-        dma_tile_block<D>(Vh, kb0, n, st + T::OFF_V, w + NW * i, lane);
+        dma_tile_block<D>(Kh, kb0, nk, st, w + NW * i, lane);
+        dma_tile_block<D>(Vh, kb0, nk, st + T::OFF_V, w + NW * i, lane);
       }
     }
   };
 
-  const int n_kt = (n + T::BCK - 1) / T::BCK;
+  const int n_kt = (nk + T::BCK - 1) / T::BCK;
+  // (The tile's last row sees the keys up to q_off + that row, q_off >= 0.)
   const int kt_end =
-      CAUSAL ? min(n_kt, (min(q0 + T::BRQ, n) - 1) / T::BCK + 1) : n_kt;
+      CAUSAL ? min(n_kt, (min(q0 + T::BRQ, n) - 1 + q_off) / T::BCK + 1) : n_kt;
   // Whether tile kt has keys after some query of this wave or past the end.
   auto needs_mask = [&](int kt) {
     const int kbase = kt * T::BCK;
-    return (CAUSAL && kbase + T::BCK - 1 > qw0) || (kbase + T::BCK > n);
+    return (CAUSAL && kbase + T::BCK - 1 > qw0 + q_off) || (kbase + T::BCK > nk);
   };
 
   // One key tile: wait for it (loaded one tile ahead) and let every wave
@@ -640,7 +648,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // Last visible key of this lane's row relative to the key in register 0
     // of block 0 (register i of block kb holds key kb*32 + (i/4)*8 + i%4
     // relative to it).
-    const int lim = (CAUSAL ? min(qrow, n - 1) : n - 1) - kbase - h * 4;
+    const int lim = (CAUSAL ? min(qrow + q_off, nk - 1) : nk - 1) - kbase - h * 4;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
@@ -785,17 +793,18 @@ hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = KVTile<D>;
-  const int n_kt = (a.n + T::BCK - 1) / T::BCK;
+  const int n_kt = (a.nk + T::BCK - 1) / T::BCK;
   // Dense causal workgroups take two key tiles each (see the kernel).
   const int units = (CAUSAL && !SPARSE) ? (n_kt + 1) / 2 : n_kt;
   const int total = (int)(a.bh * units);
   return launch_kernel(bwd_dkdv_kernel<D, CAUSAL, SPARSE, DROP>, dim3(total), dim3(512), s,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
                        (const bf16*)a.dout, (const float*)a.ws_d,
-                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt, total,
+                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, a.nk, a.q_off,
+                       n_kt, total,
                        causal_bundle(n_kt, 1), a.scale * kLog2e, a.scale,
                        a.mask, a.mask_cols, a.block_m, a.block_n,
-                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi), a.visits_kv);
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi, a.q_off), a.visits_kv);
 }
 
 // d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
@@ -811,16 +820,20 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE, DROP>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
                        (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,
-                       (const float*)a.ws_lse2, a.dq, a.n, n_qt, total,
+                       (const float*)a.ws_lse2, a.dq, a.n, a.nk, a.q_off, n_qt,
+                       total,
                        causal_bundle(n_qt, NW == 8 ? 1 : 2), a.scale * kLog2e,
                        a.scale, a.mask, a.mask_cols, a.block_m, a.block_n,
-                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi), a.visits_q);
+                       make_dropout(a.drop_t, a.seed_lo, a.seed_hi, a.q_off), a.visits_q);
 }
 
-// Block-sparse, dropout (dense only) or neither.
+// Block-sparse and/or dropout, or neither.
 template <int D>
 hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
   if (a.mask) {
+    if (a.drop_t > 0) {
+      return a.causal ? dkdv_t<D, true, true, true>(a, s) : dkdv_t<D, false, true, true>(a, s);
+    }
     return a.causal ? dkdv_t<D, true, true, false>(a, s) : dkdv_t<D, false, true, false>(a, s);
   }
   if (a.drop_t > 0) {
@@ -831,6 +844,9 @@ hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
   if (a.mask) {
+    if (a.drop_t > 0) {
+      return a.causal ? dq_t<D, true, true, true>(a, s) : dq_t<D, false, true, true>(a, s);
+    }
     return a.causal ? dq_t<D, true, true, false>(a, s) : dq_t<D, false, true, false>(a, s);
   }
   if (a.drop_t > 0) {

@@ -112,7 +112,8 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
                          const float* __restrict__ V, const float* __restrict__ dO,
                          const float* __restrict__ ws_d,
                          const float* __restrict__ ws_lse2, float* __restrict__ dK,
-                         float* __restrict__ dV, int n, int n_ktiles, float c_log2,
+                         float* __restrict__ dV, int n, int nk, int q_off,
+                         int n_ktiles, float c_log2,
                          float scale, const uint8_t* __restrict__ mask,
                          int mask_cols, int block_m, int block_n) {
   using T = F32BwdTile<D>;
@@ -126,13 +127,14 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   const int k0 = (blockIdx.x % n_ktiles) * T::ROWS;
   const int key = k0 + tid / T::TPR;
   const int c0 = part * 32;
-  const int64_t hoff = (int64_t)head * n * D;
+  const int64_t hoff = (int64_t)head * n * D;     // Q, dO: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V, dK, dV: nk rows
   const float* Lh = ws_lse2 + (int64_t)head * n;
   const float* Dh = ws_d + (int64_t)head * n;
 
   float k[32], v[32], dk[32], dv[32];
-  load32(K + hoff, key, n, D, c0, k);
-  load32(V + hoff, key, n, D, c0, v);
+  load32(K + hoff_k, key, nk, D, c0, k);
+  load32(V + hoff_k, key, nk, D, c0, v);
 #pragma unroll
   for (int c = 0; c < 32; ++c) {
     dk[c] = 0.f;
@@ -140,7 +142,8 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   }
 
   const int n_qt = (n + T::BT - 1) / T::BT;
-  const int qt0 = CAUSAL ? k0 / T::BT : 0;
+  // Under the causal rule query row i sees key k0 from i = k0 - q_off on.
+  const int qt0 = CAUSAL ? max(0, k0 - q_off) / T::BT : 0;
   for (int qt = qt0; qt < n_qt; ++qt) {
     const int q0 = qt * T::BT;
     if (SPARSE && mask[(int64_t)(q0 / block_m) * mask_cols + k0 / block_n] == 0) {
@@ -168,7 +171,7 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
       const float s = dot32<T::TPR>(k, sQ + i * D + c0);
       const float dp = dot32<T::TPR>(v, sdO + i * D + c0);
       const int q = q0 + i;
-      const bool vis = (key < n) && (!CAUSAL || key <= q);
+      const bool vis = (key < nk) && (!CAUSAL || key <= q_off + q);
       const float p = vis ? fast_exp2(fmaf(s, c_log2, -sL[i])) : 0.f;
       const float ds = p * (dp - sD[i]);
       const float* qr = sQ + i * D + c0;
@@ -185,9 +188,9 @@ void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
       }
     }
   }
-  if (key < n) {
-    store32(dK + hoff, key, D, c0, dk, scale);
-    store32(dV + hoff, key, D, c0, dv, 1.f);
+  if (key < nk) {
+    store32(dK + hoff_k, key, D, c0, dk, scale);
+    store32(dV + hoff_k, key, D, c0, dv, 1.f);
   }
 }
 
@@ -200,8 +203,8 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* __restrict__ dO,
                        const float* __restrict__ ws_d,
                        const float* __restrict__ ws_lse2, float* __restrict__ dQ,
-                       int n, int n_qtiles, float c_log2, float scale,
-                       const uint8_t* __restrict__ mask, int mask_cols,
+                       int n, int nk, int q_off, int n_qtiles, float c_log2,
+                       float scale, const uint8_t* __restrict__ mask, int mask_cols,
                        int block_m, int block_n) {
   using T = F32BwdTile<D>;
   __shared__ __attribute__((aligned(16))) float sK[T::BT * D];
@@ -215,7 +218,8 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const int q0 = qt * T::ROWS;
   const int qrow = q0 + tid / T::TPR;
   const int c0 = part * 32;
-  const int64_t hoff = (int64_t)head * n * D;
+  const int64_t hoff = (int64_t)head * n * D;     // Q, dO, dQ: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V: nk rows
 
   float q[32], dout[32], dq[32];
   load32(Q + hoff, qrow, n, D, c0, q);
@@ -225,9 +229,10 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   const float lse2 = (qrow < n) ? ws_lse2[(int64_t)head * n + qrow] : INFINITY;
   const float drow = (qrow < n) ? ws_d[(int64_t)head * n + qrow] : 0.f;
 
-  const int n_kt = (n + T::BT - 1) / T::BT;
+  const int n_kt = (nk + T::BT - 1) / T::BT;
   int kt_end = n_kt;
-  if (CAUSAL) kt_end = min(n_kt, (min(q0 + T::ROWS, n) - 1) / T::BT + 1);
+  // (Row i sees the keys up to q_off + i under the causal rule, q_off >= 0.)
+  if (CAUSAL) kt_end = min(n_kt, (min(q0 + T::ROWS, n) - 1 + q_off) / T::BT + 1);
   const uint8_t* mrow =
       SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
   for (int kt = 0; kt < kt_end; ++kt) {
@@ -237,8 +242,8 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     for (int e = tid * 4; e < T::BT * D; e += 256 * 4) {
       const int row = kbase + e / D;
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (row < n) {
-        const int64_t off = hoff + (int64_t)row * D + (e % D);
+      if (row < nk) {
+        const int64_t off = hoff_k + (int64_t)row * D + (e % D);
         kx = *reinterpret_cast<const f32x4*>(K + off);
         vx = *reinterpret_cast<const f32x4*>(V + off);
       }
@@ -250,7 +255,7 @@ void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       const float s = dot32<T::TPR>(q, sK + j * D + c0);
       const float dp = dot32<T::TPR>(dout, sV + j * D + c0);
       const int key = kbase + j;
-      const bool vis = (key < n) && (!CAUSAL || key <= qrow);
+      const bool vis = (key < nk) && (!CAUSAL || key <= q_off + qrow);
       const float p = vis ? fast_exp2(fmaf(s, c_log2, -lse2)) : 0.f;
       const float ds = p * (dp - drow);
       const float* kr = sK + j * D + c0;
@@ -277,12 +282,13 @@ hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using T = F32BwdTile<D>;
-  const int n_kt = (a.n + T::ROWS - 1) / T::ROWS;
+  const int n_kt = (a.nk + T::ROWS - 1) / T::ROWS;
   return launch_kernel(bwd_dkdv_f32_kernel<D, CAUSAL, SPARSE>,
                        dim3((unsigned)(a.bh * n_kt)), dim3(256), s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v,
                        (const float*)a.dout, (const float*)a.ws_d,
-                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, n_kt,
+                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, a.nk, a.q_off,
+                       n_kt,
                        a.scale * kLog2e, a.scale, a.mask, a.mask_cols,
                        a.block_m, a.block_n);
 }
@@ -295,7 +301,7 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
                        dim3((unsigned)(a.bh * n_qt)), dim3(256), s,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v,
                        (const float*)a.dout, (const float*)a.ws_d,
-                       (const float*)a.ws_lse2, a.dq, a.n, n_qt,
+                       (const float*)a.ws_lse2, a.dq, a.n, a.nk, a.q_off, n_qt,
                        a.scale * kLog2e, a.scale, a.mask, a.mask_cols,
                        a.block_m, a.block_n);
 }

@@ -224,20 +224,25 @@ inline int causal_bundle(int n_tiles, int wgs_per_cu) {
 // the steps fused into the attention kernel).  The random numbers come from
 // the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
 // "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).  Element (bh, i,
-// j) of head bh, query i and key j takes byte (j & 3) of word (i & 3) of the
-// call with counter (i >> 2, j >> 2, bh, 0) and key (seed low, seed high);
-// it is kept iff that byte is >= t (drop probability t / 256).  One call
-// covers a 4 x 4 block of scores, so the mask does not depend on the tiling.
+// j) of head bh, query row i and key j takes byte (j & 3) of word (i & 3) of
+// the call with counter (i >> 2, j >> 2, bh, off) and key (seed low, seed
+// high), off being the position of query row 0 among the keys (0 when
+// queries and keys are the same tokens); it is kept iff that byte is >= t
+// (drop probability t / 256).  One call covers a 4 x 4 block of scores, so
+// the mask does not depend on the tiling.
 // ---------------------------------------------------------------------------
 struct Dropout {
   uint32_t k0, k1;  // seed words
   uint32_t bh;      // head index b * H + h
   uint32_t t;       // keep iff byte >= t
   float inv_keep;   // 256 / (256 - t)
+  uint32_t off;     // counter word 3: position of query row 0
 };
 
-inline Dropout make_dropout(int t, uint32_t seed_lo, uint32_t seed_hi) {
-  return Dropout{seed_lo, seed_hi, 0u, (uint32_t)t, 256.f / (float)(256 - t)};
+inline Dropout make_dropout(int t, uint32_t seed_lo, uint32_t seed_hi,
+                            int q_off) {
+  return Dropout{seed_lo, seed_hi, 0u, (uint32_t)t, 256.f / (float)(256 - t),
+                 (uint32_t)q_off};
 }
 
 // One Philox4x32-10 call: ten rounds of two 32 x 32 -> 64-bit products with
@@ -295,7 +300,7 @@ __device__ __forceinline__ void dropout_bytes_rowlane(const Dropout& dr, int row
   out[0] = (uint32_t)row >> 2;
   out[1] = (uint32_t)(key0 + 8 * q + 4 * h) >> 2;
   out[2] = dr.bh;
-  out[3] = 0;
+  out[3] = dr.off;
   philox4x32_10(out, dr.k0, dr.k1);
   // ... whose word q' belongs to row 4 (row >> 2) + q', the lane q' of the quad
   quad_transpose(out, lane);
@@ -310,7 +315,7 @@ __device__ __forceinline__ void dropout_bytes_keylane(const Dropout& dr, int key
                                                       uint32_t (&out)[4]) {
   const int h = (lane >> 5) & 1, q = lane & 3;
   uint32_t x[4] = {(uint32_t)(row0 + 8 * q + 4 * h) >> 2, (uint32_t)key >> 2,
-                   dr.bh, 0};
+                   dr.bh, dr.off};
   philox4x32_10(x, dr.k0, dr.k1);
   // word u of x belongs to query row0 + 8 q + 4 h + u and holds the four
   // keys of the quad in its bytes; regroup so that word c holds key c's

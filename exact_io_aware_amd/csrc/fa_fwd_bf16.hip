@@ -273,7 +273,7 @@ struct FwdWave {
     for (int kb = 0; kb < T::KB; ++kb) {
       uint32_t u[4];
       if constexpr (DROP)
-        dropout_bytes_rowlane(dr, q_off + qrow, kbase + kb * 32, __lane_id(), u);
+        dropout_bytes_rowlane(dr, qrow, kbase + kb * 32, __lane_id(), u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
@@ -470,7 +470,8 @@ template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP, bool COUNT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
-                     float* __restrict__ LSE, int n, int n_qtiles, int total,
+                     float* __restrict__ LSE, int n, int nk, int q_off,
+                     int n_qtiles, int total,
                      int bundle, float c_log2, const uint8_t* __restrict__ mask,
                      int mask_cols, int block_m, int block_n, Dropout drop,
                      int* __restrict__ visits) {
@@ -500,22 +501,26 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   } else {
     pl = fwd_place<CAUSAL>(n_qtiles, total, T::BR, bundle);
   }
-  const int64_t hoff = (int64_t)pl.head * n * D;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
+  const int64_t hoff = (int64_t)pl.head * n * D;  // Q, O: n rows per head
+  const int64_t hoff_k = (int64_t)pl.head * nk * D;  // K, V: nk rows
+  const bf16* Kh = K + hoff_k;
+  const bf16* Vh = V + hoff_k;
   const TileFill<T> fill(w, lane);
-  const int n_ktiles = (n + T::BC - 1) / T::BC;
+  const int n_ktiles = (nk + T::BC - 1) / T::BC;
 
   // One query tile of 32 * NW rows from row q0.
   auto run_tile = [&](int q0) {
-    FwdWave<T, CAUSAL, DROP> wv(Q + hoff, q0 + 32 * w, lane, n, n, 0, c_log2);
+    FwdWave<T, CAUSAL, DROP> wv(Q + hoff, q0 + 32 * w, lane, n, nk, q_off,
+                                c_log2);
     if constexpr (DROP) {
       wv.dr = drop;
       wv.dr.bh = (uint32_t)pl.head;
     }
     // Key tiles to visit, in order.
     int kt_end = n_ktiles;
-    if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::BR, n) - 1) / T::BC + 1);
+    // (Under the causal rule the tile's last row sees the keys up to
+    // q_off + that row, q_off >= 0.)
+    if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::BR, n) - 1 + q_off) / T::BC + 1);
     // Block-sparse: the mask row of this workgroup's block row (a 64-entry
     // window at a time).  A key tile lies in one mask column.
     MaskLine mline(SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : mask,
@@ -535,7 +540,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       return __builtin_amdgcn_readfirstlane(kt);
     };
     int nvis = 0;
-    key_loop(wv, fill, kbuf, vbuf, Kh, Vh, n, next_on(-1), kt_end, next_on,
+    key_loop(wv, fill, kbuf, vbuf, Kh, Vh, nk, next_on(-1), kt_end, next_on,
              nvis);
     wv.store(O + hoff, LSE + (int64_t)pl.head * n);
     // Diagnostic count of the key tiles this query tile visited (COUNT
@@ -563,9 +568,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int bundle = causal_bundle(n_qtiles, NW == 8 ? 1 : 2);
   return launch_kernel(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, DROP, COUNT>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, n_qtiles,
-                       total, bundle, a.scale * kLog2e, a.mask, a.mask_cols,
-                       a.block_m, a.block_n, make_dropout(a.drop_t, a.seed_lo, a.seed_hi),
+                       (const bf16*)a.v, (bf16*)a.o, a.lse, a.n, a.nk, a.q_off,
+                       n_qtiles, total, bundle, a.scale * kLog2e, a.mask, a.mask_cols,
+                       a.block_m, a.block_n, make_dropout(a.drop_t, a.seed_lo, a.seed_hi, a.q_off),
                        a.visits);
 }
 
@@ -579,7 +584,11 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
     return a.causal ? launch_fwd<D, true, false, false, true>(a, s)
                     : launch_fwd<D, false, false, false, true>(a, s);
   }
-  if (a.mask) {  // (no dropout with a block mask)
+  if (a.mask) {
+    if (a.drop_t > 0) {
+      return a.causal ? launch_fwd<D, true, true, true>(a, s)
+                      : launch_fwd<D, false, true, true>(a, s);
+    }
     return a.causal ? launch_fwd<D, true, true, false>(a, s)
                     : launch_fwd<D, false, true, false>(a, s);
   }

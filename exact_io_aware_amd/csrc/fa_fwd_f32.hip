@@ -44,8 +44,8 @@ template <int D, bool CAUSAL, bool SPARSE, int KSPLIT>
 __global__ __launch_bounds__(256)
 void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, float* __restrict__ O,
-                    float* __restrict__ LSE, int n, int n_qtiles,
-                    float c_log2, const uint8_t* __restrict__ mask,
+                    float* __restrict__ LSE, int n, int nk, int q_off,
+                    int n_qtiles, float c_log2, const uint8_t* __restrict__ mask,
                     int mask_cols, int block_m, int block_n) {
   using T = F32Tile<D, KSPLIT>;
   __shared__ __attribute__((aligned(16))) float smem[2 * T::BC * D];
@@ -61,7 +61,8 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                         : (blockIdx.x % n_qtiles);
   const int q0 = qt * T::ROWS;
   const int qrow = q0 + gtid / T::TPR;
-  const int64_t hoff = (int64_t)head * n * D;
+  const int64_t hoff = (int64_t)head * n * D;     // Q, O: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V: nk rows
   const int c0 = part * 32;  // first d coordinate owned by this lane
 
   float q[32], acc[32];
@@ -80,9 +81,10 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
   for (int c = 0; c < 32; ++c) acc[c] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int n_ktiles = (n + T::BC - 1) / T::BC;
+  const int n_ktiles = (nk + T::BC - 1) / T::BC;
   int kt_end = n_ktiles;
-  if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::ROWS, n) - 1) / T::BC + 1);
+  // (Row i sees the keys up to q_off + i under the causal rule, q_off >= 0.)
+  if (CAUSAL) kt_end = min(n_ktiles, (min(q0 + T::ROWS, n) - 1 + q_off) / T::BC + 1);
   const uint8_t* mrow =
       SPARSE ? mask + (int64_t)(q0 / block_m) * mask_cols : nullptr;
 
@@ -93,8 +95,8 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     for (int e = tid * 4; e < T::BC * D; e += 256 * 4) {
       const int row = e / D;
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (kbase + row < n) {
-        const int64_t off = hoff + (int64_t)(kbase + row) * D + (e % D);
+      if (kbase + row < nk) {
+        const int64_t off = hoff_k + (int64_t)(kbase + row) * D + (e % D);
         kx = *reinterpret_cast<const f32x4*>(K + off);
         vx = *reinterpret_cast<const f32x4*>(V + off);
       }
@@ -102,7 +104,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
       *reinterpret_cast<f32x4*>(sV + e) = vx;
     }
     __syncthreads();
-    const int kend = min(T::BC, n - kbase);
+    const int kend = min(T::BC, nk - kbase);
     for (int k0 = grp * T::CH; k0 < kend; k0 += T::CH * KSPLIT) {
       float s[T::CH];
 #pragma unroll
@@ -120,7 +122,7 @@ void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         if constexpr (T::TPR >= 2) dot += __shfl_xor(dot, 1);
         if constexpr (T::TPR >= 4) dot += __shfl_xor(dot, 2);
         const int key = kbase + k0 + j;
-        s[j] = ((CAUSAL && key > qrow) || key >= n) ? -INFINITY : dot;
+        s[j] = ((CAUSAL && key > q_off + qrow) || key >= nk) ? -INFINITY : dot;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -215,7 +217,8 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
   const int total = (int)(a.bh * n_qtiles);
   return launch_kernel(fwd_f32_kernel<D, CAUSAL, SPARSE, KSPLIT>, dim3(total),
                        dim3(256), s, (const float*)a.q, (const float*)a.k,
-                       (const float*)a.v, (float*)a.o, a.lse, a.n, n_qtiles,
+                       (const float*)a.v, (float*)a.o, a.lse, a.n, a.nk, a.q_off,
+                       n_qtiles,
                        a.scale * kLog2e, a.mask, a.mask_cols, a.block_m,
                        a.block_n);
 }

@@ -16,15 +16,18 @@ struct FwdArgs {
   void* o;
   float* lse;
   int64_t bh;              // B * H
-  int n;                   // sequence length
+  int n;                   // query rows
+  int nk;                  // keys
+  int q_off;               // position of query row 0 among the keys (causal
+                           // rule: key j visible to row i iff j <= q_off + i)
   int d;                   // head dim (64 or 128)
   float scale;             // > 0
   int causal;
   const uint8_t* mask;     // nullptr = dense
-  int mask_cols;           // ceil(n / block_n)
+  int mask_cols;           // ceil(nk / block_n)
   int block_m;             // multiple of 128
   int block_n;             // multiple of 128
-  int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
+  int drop_t = 0;          // dropout threshold t (0 = no dropout; bf16 only)
   uint32_t seed_lo = 0;    // dropout seed words
   uint32_t seed_hi = 0;
   int* visits = nullptr;   // diagnostic: key tiles visited per query tile
@@ -40,18 +43,20 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* ws_d;             // B*H*N: rowsum(dO * O)
-  float* ws_lse2;          // B*H*N: lse * log2(e), +inf for empty rows
+  float* ws_d;             // B*H*n: rowsum(dO * O)
+  float* ws_lse2;          // B*H*n: lse * log2(e), +inf for empty rows
   int64_t bh;
-  int n;
+  int n;                   // query rows
+  int nk;                  // keys
+  int q_off;               // as FwdArgs::q_off
   int d;
   float scale;
   int causal;
   const uint8_t* mask;     // nullptr = dense
-  int mask_cols;           // ceil(n / block_n)
+  int mask_cols;           // ceil(nk / block_n)
   int block_m;             // multiple of 128
   int block_n;             // multiple of 128
-  int drop_t = 0;          // dropout threshold t (0 = no dropout; dense bf16 only)
+  int drop_t = 0;          // dropout threshold t (0 = no dropout; bf16 only)
   uint32_t seed_lo = 0;    // dropout seed words
   uint32_t seed_hi = 0;
   int* visits_kv = nullptr;  // diagnostic: query tiles visited per key tile

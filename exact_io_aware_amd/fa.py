@@ -77,6 +77,10 @@ def declare(lib):
                            I64, I, F, I, F, U64, P],
         "fa_bwd_noalloc": [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I,
                            F, I, P],
+        "fa_fwd_general": [P, P, P, P, P, I64, I64, I64, I64, I64, I, F, I,
+                           P, I64, I64, F, U64, P],
+        "fa_bwd_general": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
+                           I64, I64, I, F, I, P, I64, I64, F, U64, P],
         "fa_tile_grid": [I, I64, I, P, P],
         "fa_fwd_tile_visits": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, P,
                                I64, I64, P, SZ, P],
@@ -209,12 +213,13 @@ def _grads(q, dq, dk, dv):
     return res
 
 
-def _mask_arg(block_mask, N, block_m, block_n, device):
-    """The block mask as a contiguous uint8 device tensor (or None)."""
+def _mask_arg(block_mask, N, block_m, block_n, device, Nk=None):
+    """The block mask as a contiguous uint8 device tensor (or None); its
+    shape is ceil(N / block_m) x ceil(Nk / block_n), Nk = N by default."""
     if block_mask is None:
         return None
     rows = -(-N // int(block_m))
-    cols = -(-N // int(block_n))
+    cols = -(-(N if Nk is None else Nk) // int(block_n))
     if tuple(block_mask.shape) != (rows, cols):
         raise ValueError(f"block mask must be {rows} x {cols}, got "
                          f"{tuple(block_mask.shape)}")
@@ -389,6 +394,76 @@ def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, block_m=128,
             _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, B, H, N, d, _dtype_code(q),
             _scale(scale, d), int(bool(causal)), _ptr(mask_t), int(block_m),
             int(block_n), _stream(q.device)))
+    return dq, dk, dv
+
+
+def _qk_shapes(q, k, v, o=None, do=None):
+    """(B, H, Nq, Nk, d) of a call with Nq query rows and Nk key rows:
+    q (and o, do) B x H x Nq x d, k and v B x H x Nk x d, one dtype and
+    device, contiguous."""
+    B, H, Nk, d = _shape4(k, v)
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        if t is None:
+            continue
+        if t.dim() != 4 or tuple(t.shape[:2]) != (B, H) or t.shape[3] != d:
+            raise ValueError(f"{name} must be B x H x Nq x d with B, H, d of "
+                             f"k; got {tuple(t.shape)}")
+        if t.dtype != k.dtype or t.device != k.device:
+            raise ValueError(f"{name} must share k's dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    Nq = q.shape[2]
+    for name, t in (("o", o), ("do", do)):
+        if t is not None and t.shape[2] != Nq:
+            raise ValueError(f"{name} must have q's {Nq} rows")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_general(q, k, v, scale=None, causal=False, block_mask=None,
+                   block_m=128, block_n=128, p_drop=0.0, seed=0, out=None,
+                   lse=None):
+    """The forward with every option together: q is B x H x Nq x d, k and v
+    B x H x Nk x d; under the causal rule the queries are the last Nq of the
+    Nk tokens (query i sees key j iff j <= Nk - Nq + i); an optional block
+    mask of shape (ceil(Nq / block_m), ceil(Nk / block_n)); dropout with
+    probability round(256 p_drop) / 256 (bf16 only)."""
+    B, H, Nq, Nk, d = _qk_shapes(q, k, v)
+    lib = library()
+    mask_t = _mask_arg(block_mask, Nq, block_m, block_n, q.device, Nk)
+    o, lse_t = _fwd_outputs(q, (B, H, Nq, d), out, lse)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_general(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Nq, Nk, d,
+            _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(mask_t),
+            int(block_m), int(block_n), float(p_drop),
+            int(seed) & (2**64 - 1), _stream(q.device)))
+    return o, lse_t
+
+
+def fa_bwd_general(q, k, v, o, do, lse, scale=None, causal=False,
+                   block_mask=None, block_m=128, block_n=128, p_drop=0.0,
+                   seed=0, workspace=None, dq=None, dk=None, dv=None):
+    """dQ (B x H x Nq x d), dK and dV (B x H x Nk x d), float32, of
+    ``fa_fwd_general`` with the same arguments (o, lse from it)."""
+    B, H, Nq, Nk, d = _qk_shapes(q, k, v, o, do)
+    lib = library()
+    mask_t = _mask_arg(block_mask, Nq, block_m, block_n, q.device, Nk)
+    _arg(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    else:
+        _arg(dq, "dq", q.shape, torch.float32, q.device)
+    dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=q.device)
+              if t is None else _arg(t, name, k.shape, torch.float32, q.device)
+              for name, t in (("dk", dk), ("dv", dv)))
+    ws, ws_bytes = _workspace(B, H, Nq, d, q.device, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_general(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, B, H, Nq, Nk, d,
+            _dtype_code(q), _scale(scale, d), int(bool(causal)), _ptr(mask_t),
+            int(block_m), int(block_n), float(p_drop),
+            int(seed) & (2**64 - 1), _stream(q.device)))
     return dq, dk, dv
 
 

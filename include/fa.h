@@ -22,7 +22,8 @@
  *   B x H x N x d (d fastest, no padding): element (b, h, i, c) sits at
  *   offset ((b*H + h)*N + i)*d + c.  LSE and the backward workspace rows are
  *   B x H x N float32 arrays in the same (b, h, i) order.  Queries and keys
- *   have the same length N (except in fa_fwd_splitkv).
+ *   have the same length N, except in fa_fwd_splitkv, fa_fwd_general and
+ *   fa_bwd_general (Nq query rows, Nk key rows).
  * Pointers.  Every tensor pointer is a device pointer owned by the caller,
  *   aligned to 16 bytes.  The library allocates no device memory; its only
  *   global state is the per-device address of the scratch array of
@@ -229,8 +230,9 @@ fa_status fa_bwd_blocksparse(const void* q, const void* k, const void* v,
  *            the launch configuration; call fa_bwd_dropout with the same
  *            seed and p_drop.
  * Other arguments, outputs and errors as fa_fwd.  FA_BF16 only (FA_F32
- * returns FA_ERR_UNSUPPORTED); no block mask.  (The shape limits shared by
- * every call keep B*H below 2^31, so bh always fits its counter word.)
+ * returns FA_ERR_UNSUPPORTED); for dropout with a block mask or with Nq !=
+ * Nk see fa_fwd_general.  (The shape limits shared by every call keep B*H
+ * below 2^31, so bh always fits its counter word.)
  */
 fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
                          float* lse, int64_t B, int64_t H, int64_t N,
@@ -280,8 +282,56 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v,
                          int64_t H, int64_t N, int64_t d, fa_dtype dt,
                          float scale, int causal, void* stream);
 
+/*
+ * fa_fwd_general / fa_bwd_general — the forward and backward with every
+ * option of the other calls available together:
+ *   * Nq queries against Nk keys.  Under the causal rule the queries are
+ *     the last Nq of the Nk tokens: query row i sits at position
+ *     Nk - Nq + i and sees key j iff j <= Nk - Nq + i (a prompt fed in
+ *     chunks against the keys of the chunks before it, or a decoding step;
+ *     [REAPER] section 3.6).  With Nq = Nk this is fa_fwd's causal rule.
+ *   * an optional block mask (mask != NULL), as fa_fwd_blocksparse but of
+ *     shape ceil(Nq / block_m) x ceil(Nk / block_n); key j is visible to
+ *     query i iff mask[i / block_m][j / block_n] != 0 AND the causal rule;
+ *     block_m and block_n are ignored when mask == NULL.
+ *   * optional dropout (p_drop > 0), as fa_fwd_dropout, with the counter
+ *     of element (bh, i, j) set to (i >> 2, j >> 2, bh, (Nk - Nq) mod 2^32),
+ *     i the row of Q: chunks at different offsets draw disjoint random
+ *     numbers, and Nq = Nk gives fa_fwd_dropout's mask.  bf16 only
+ *     (FA_F32 with p_drop > 0 returns FA_ERR_UNSUPPORTED).
+ * A row that sees no key gets O = 0, lse = -inf and dQ = 0; a key that no
+ * query sees gets dK = dV = 0.
+ *
+ * q, o, dout : B x H x Nq x d, dtype `dt`;  k, v : B x H x Nk x d, dtype dt.
+ * lse        : B x H x Nq float32.
+ * dq         : B x H x Nq x d float32;  dk, dv : B x H x Nk x d float32.
+ * workspace  : at least fa_bwd_workspace_bytes(B, H, Nq, d) bytes (the
+ *              per-row workspace is per query row).
+ * Sizes: B, H, Nq >= 0 (any of them 0: nothing to do, FA_OK); otherwise
+ * 1 <= Nk <= 2^30, and Nq <= Nk when causal != 0 (else FA_ERR_SHAPE).
+ * fa_bwd_general takes o and lse from fa_fwd_general with the same
+ * arguments.  Other arguments and errors as fa_fwd / fa_bwd (FA_ERR_MASK
+ * for invalid block sizes with a mask, FA_ERR_ARG for p_drop outside
+ * [0, 255/256]).  With Nq = Nk, mask == NULL and p_drop = 0 the results
+ * equal fa_fwd / fa_bwd bitwise.
+ */
+fa_status fa_fwd_general(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t Nq,
+                         int64_t Nk, int64_t d, fa_dtype dt, float scale,
+                         int causal, const uint8_t* mask, int64_t block_m,
+                         int64_t block_n, float p_drop, uint64_t seed,
+                         void* stream);
+fa_status fa_bwd_general(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, fa_dtype dt,
+                         float scale, int causal, const uint8_t* mask,
+                         int64_t block_m, int64_t block_n, float p_drop,
+                         uint64_t seed, void* stream);
+
 /* Bytes of workspace fa_bwd and fa_bwd_blocksparse need (0 for empty
- * problems). */
+ * problems); fa_bwd_general needs fa_bwd_workspace_bytes(B, H, Nq, d). */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*

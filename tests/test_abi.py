@@ -372,3 +372,50 @@ def test_tile_visits_validation(lib):
     assert bwdv(nkv=2 * 8 - 1) == FA_ERR_ARG        # 2 heads x 8 key tiles
     assert bwdv(nq=2 * 4 - 1) == FA_ERR_ARG         # 2 heads x 4 query tiles
     assert bwdv(ws=16) == FA_ERR_ARG
+
+
+def fwd_gen(lib, q=P, B=1, H=2, Nq=100, Nk=300, d=128, dt=BF16, scale=0.1,
+            causal=1, mask=None, bm=128, bn=128, p=0.0, seed=3):
+    return lib.fa_fwd_general(q, P, P, P, P, B, H, Nq, Nk, d, dt, scale,
+                              causal, mask, bm, bn, p, seed, None)
+
+
+def bwd_gen(lib, ws=P, ws_bytes=1 << 20, B=1, H=2, Nq=100, Nk=300, d=128,
+            dt=BF16, causal=1, mask=None, bm=128, bn=128, p=0.0, dq=P):
+    return lib.fa_bwd_general(P, P, P, P, P, P, dq, P, P, ws, ws_bytes, B, H,
+                              Nq, Nk, d, dt, 0.1, causal, mask, bm, bn, p, 7,
+                              None)
+
+
+def test_general_validation(lib):
+    """fa_fwd_general / fa_bwd_general: key length 1..2^30, Nq <= Nk under
+    the causal rule (any lengths otherwise), block sizes checked only with a
+    mask, dropout bf16 only and in range, the workspace sized by query
+    rows; the shared checks keep their codes."""
+    # Non-causal calls take any lengths: the shape passes, the NULL pointer
+    # checked after it is what fails.
+    assert fwd_gen(lib, Nq=301, Nk=300, causal=0, q=None) == FA_ERR_NULL
+    assert bwd_gen(lib, Nq=301, Nk=300, causal=0, ws=None) == FA_ERR_NULL
+    for f in (fwd_gen, bwd_gen):
+        assert f(lib, Nq=301, Nk=300) == FA_ERR_SHAPE      # causal: Nq <= Nk
+        assert f(lib, Nk=0) == FA_ERR_SHAPE
+        assert f(lib, Nk=-1) == FA_ERR_SHAPE
+        assert f(lib, Nk=(1 << 30) + 1) == FA_ERR_SHAPE
+        assert f(lib, Nq=-1) == FA_ERR_SHAPE
+        assert f(lib, d=96) == FA_ERR_UNSUPPORTED
+        assert f(lib, mask=P, bm=64) == FA_ERR_MASK
+        assert f(lib, mask=P, bn=100) == FA_ERR_MASK
+        assert f(lib, p=-0.5) == FA_ERR_ARG
+        assert f(lib, p=1.0) == FA_ERR_ARG
+        assert f(lib, p=0.2, dt=F32) == FA_ERR_UNSUPPORTED
+        assert f(lib, B=0) == FA_OK                         # empty: no-op
+        assert f(lib, Nq=0, Nk=0) == FA_OK
+    assert fwd_gen(lib, q=None) == FA_ERR_NULL
+    assert fwd_gen(lib, q=MISALIGNED) == FA_ERR_ALIGN
+    assert fwd_gen(lib, scale=0.0) == FA_ERR_ARG
+    assert bwd_gen(lib, ws=None) == FA_ERR_NULL
+    assert bwd_gen(lib, dq=None) == FA_ERR_NULL
+    # The workspace is per query row: enough for Nq rows, too small for Nk.
+    need = lib.fa_bwd_workspace_bytes(1, 2, 100, 128)
+    assert need < lib.fa_bwd_workspace_bytes(1, 2, 300, 128)
+    assert bwd_gen(lib, ws_bytes=need - 1) == FA_ERR_ARG
