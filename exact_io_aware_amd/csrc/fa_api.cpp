@@ -572,7 +572,7 @@ fa_status fa_tile_grid(int pass, int64_t d, int sparse, int64_t* rows,
   int r = 0, c = 0;
   switch (pass) {
     case 0: fa::fwd_bf16_tile_grid((int)d, sparse != 0, &r, &c); break;
-    case 1: fa::bwd_dkdv_tile_grid((int)d, &r, &c); break;
+    case 1: fa::bwd_dkdv_tile_grid((int)d, sparse != 0, &r, &c); break;
     case 2: fa::bwd_dq_tile_grid((int)d, sparse != 0, &r, &c); break;
     default: return FA_ERR_ARG;
   }
@@ -613,7 +613,7 @@ fa_status fa_bwd_tile_visits(const void* q, const void* k, const void* v,
   if (!visits_kv || !visits_q) return FA_ERR_NULL;
   if (!aligned(visits_kv, 4) || !aligned(visits_q, 4)) return FA_ERR_ALIGN;
   int rows = 0, cols = 0;
-  fa::bwd_dkdv_tile_grid((int)d, &rows, &cols);
+  fa::bwd_dkdv_tile_grid((int)d, mask != nullptr, &rows, &cols);
   if (kv_len < (size_t)(a.bh * ((N + cols - 1) / cols))) return FA_ERR_ARG;
   fa::bwd_dq_tile_grid((int)d, mask != nullptr, &rows, &cols);
   if (q_len < (size_t)(a.bh * ((N + rows - 1) / rows))) return FA_ERR_ARG;

@@ -482,6 +482,316 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
+// dkdv pass, d = 128 without mask or dropout: 256 keys per workgroup
+// ---------------------------------------------------------------------------
+// Each staged query tile serves 256 keys instead of 128, which halves the
+// bytes moved into LDS per key.  K and V of the 256 keys fill 128 KB of LDS
+// (each key's K row followed by its V row, so that the V operand is the K
+// address plus an immediate), two 32-query stages of Q and dO the other
+// 32 KB.  That leaves no LDS for the per-row statistics, and in the S = Q K^T
+// layout a lane would need them for 16 query rows; instead they enter the
+// products: one more k-step of 16 adds -lse2_i / c to S_ij (A operand: the
+// value split into two bf16 parts in slots 0 and 1 of query i's lane, B:
+// ones) and one adds -D_i to dP_ij, so that P = exp2(c S') and dS = P dP'.
+// The two bf16 parts carry 16 significant bits (relative error ~2^-17,
+// against the 2^-9 of the bf16 P and dS).  Wave w owns keys k0 + 32w .. +
+// 31 and the whole 32-query block of every stage, so no cross-wave
+// reduction is needed at the end.
+struct KV256Tile {
+  static constexpr int D = 128;
+  static constexpr int NW = 8;                        // waves per workgroup
+  static constexpr int BCK = 256;                     // keys per workgroup
+  static constexpr int BRQ = 32;                      // queries per LDS stage
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int ROW = D * 2;                   // one row of K, V, Q or dO
+  static constexpr int KV_ROW = 2 * ROW;              // K row, then V row, of a key
+  static constexpr int KV_BYTES = BCK * KV_ROW;
+  static constexpr int T_BYTES = BRQ * ROW;           // Q (or dO) of one stage
+  // LDS: K/V rows | stage 0 | stage 1; stage = Q | dO
+  static constexpr int OFF_ST = KV_BYTES;
+  static constexpr int S_DO = T_BYTES;
+  static constexpr int STAGE = 2 * T_BYTES;
+  static constexpr int LDS = OFF_ST + 2 * STAGE;
+  static constexpr int KV_BLK = KV_BYTES / 1024 / NW;  // 1-KB DMA blocks per wave
+  static constexpr int T_BLK = T_BYTES / 1024 / NW;
+  static_assert(LDS <= 160 * 1024, "fits the LDS of a CU");
+  static_assert(KV_BLK * NW * 1024 == KV_BYTES && T_BLK * NW * 1024 == T_BYTES,
+                "tiles split evenly into 1-KB blocks per wave");
+};
+
+// Element `off` of a buffer of `n` floats; past the end it reads as 0
+// (hardware range check of the buffer resource).
+__device__ __forceinline__ float load1_bounded(const float* base, int n, int off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), (short)0, n * 4, 0x00020000);
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r, off * 4, 0, 0));
+}
+
+// A operand of the extra k-step: x split into bf16 parts hi + lo in slots 0
+// and 1 of the half-wave h = 0 (slots k = 0, 1 of row l32), zeros elsewhere.
+// x = -inf gives hi = -inf, lo = 0.
+__device__ __forceinline__ bf16x8 split_operand(float x, int h) {
+  const float hi = __builtin_bit_cast(float, pack_bf16(x, 0.f) << 16);
+  const float lo = (x == -INFINITY) ? 0.f : x - hi;
+  u32x4 u = {h ? 0u : pack_bf16(hi, lo), 0u, 0u, 0u};
+  return as_bf16x8(u);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                        const float* __restrict__ ws_d,
+                        const float* __restrict__ ws_lse2,
+                        float* __restrict__ dK, float* __restrict__ dV, int n,
+                        int nk, int q_off, int n_ktiles, int total,
+                        float c_log2, float scale, int* __restrict__ visits) {
+  using T = KV256Tile;
+  constexpr int D = T::D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lid = xcd_logical_id(blockIdx.x, total);
+  // Causal: key tiles u and n_ktiles-1-u of one head per workgroup (equal
+  // work for every workgroup, as in the 128-key kernel).
+  int head, kt_a, kt_b = -1;
+  if constexpr (CAUSAL) {
+    const int units = (n_ktiles + 1) / 2;
+    const int u = lid % units;
+    head = lid / units;
+    kt_a = u;
+    if (u != n_ktiles - 1 - u) kt_b = n_ktiles - 1 - u;
+  } else {
+    head = lid / n_ktiles;
+    kt_a = lid % n_ktiles;
+  }
+  const int64_t hoff = (int64_t)head * n * D;     // Q, dO: n rows per head
+  const int64_t hoff_k = (int64_t)head * nk * D;  // K, V, dK, dV: nk rows
+  const float* Lh = ws_lse2 + (int64_t)head * n;
+  const float* Dh = ws_d + (int64_t)head * n;
+
+  auto run_tile = [&](int kt) {
+  const int k0 = kt * T::BCK;
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+
+  // K and V rows of the workgroup's keys (rows past the end read row
+  // nk - 1; their dK, dV are never stored).  Lane `lane` of 1-KB block b
+  // fills bytes 16*lane of it: key 2b + lane/32, the K row for lanes
+  // 0-15 and 32-47, the V row for the others, physical chunk = logical
+  // chunk ^ swizzle of the key.
+#pragma unroll
+  for (int i = 0; i < T::KV_BLK; ++i) {
+    const int b = w + T::NW * i;
+    const int kr = 2 * b + (lane >> 5);
+    const bf16* src = ((lane >> 4) & 1) ? V : K;
+    const int c = (lane & 15) ^ tile_swz<D>(kr);
+    dma16(src + hoff_k + (int64_t)min(k0 + kr, nk - 1) * D + c * 8,
+          smem + b * 1024);
+  }
+
+  const int n_qt = (n + T::BRQ - 1) / T::BRQ;
+  // Under the causal rule query row i sees key k0 from i = k0 - q_off on.
+  const int qt_begin = CAUSAL ? max(0, k0 - q_off) / T::BRQ : 0;
+  // Stage sources: lane `lane` fills bytes 16*lane of 1-KB block w of the
+  // Q (dO) tile: row o / ROW, physical chunk = logical chunk ^ swizzle.
+  const int o_st = w * 1024 + lane * 16;
+  const int st_row = o_st / T::ROW;
+  const int goff = st_row * D + ((((o_st % T::ROW) >> 4) ^ tile_swz<D>(st_row)) * 8);
+  auto issue_stage = [&](int qt, int stage) {
+    unsigned char* st = smem + T::OFF_ST + stage * T::STAGE + w * 1024;
+    const int q0 = qt * T::BRQ;
+    if (q0 + T::BRQ <= n) {
+      dma16(Q + hoff + (int64_t)q0 * D + (uint32_t)goff, st);
+      dma16(dO + hoff + (int64_t)q0 * D + (uint32_t)goff, st + T::S_DO);
+    } else {
+      dma_tile_block<D>(Q + hoff, q0, n, smem + T::OFF_ST + stage * T::STAGE, w, lane);
+      dma_tile_block<D>(dO + hoff, q0, n, smem + T::OFF_ST + stage * T::STAGE + T::S_DO,
+                        w, lane);
+    }
+  };
+
+  f32x16 adk[T::DB], adv[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    adk[db] = zero16();
+    adv[db] = zero16();
+  }
+  // LDS offsets: aK the row-wise K operand (key w*32 + l32, chunk
+  // ks*2 + h; + ROW: the V operand); aQ the row-wise Q (+ S_DO: dO) operand
+  // of stage 0; aT the transposed reads of stage 0.
+  // (The swizzle of key row w*32 + l32 equals that of Q row l32, so aQ is
+  // aK plus one per-lane difference: one add per read, 7 registers fewer.)
+  int aK[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    const int kr = w * 32 + l32;
+    aK[ks] = kr * T::KV_ROW + (((ks * 2 + h) ^ tile_swz<D>(kr)) << 4);
+  }
+  const int q_minus_k = T::OFF_ST + l32 * T::ROW - (w * 32 + l32) * T::KV_ROW;
+  // B operand of the extra k-steps: ones in slots k = 0, 1 (half-wave 0).
+  const bf16x8 ones = as_bf16x8(u32x4{h ? 0u : 0x3f803f80u, 0u, 0u, 0u});
+  const float neg_inv_c = -1.f / c_log2;
+  int aT[T::DB][2];
+  tr_offsets<D, T::DB>(lane, aT);
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) {
+    aT[db][0] += T::OFF_ST;
+    aT[db][1] += T::OFF_ST;
+  }
+
+  int nvis = 0;  // query tiles visited (diagnostic count)
+  // Query row qq0 + l32's statistics, loaded one stage ahead (rows past the
+  // end read 0 and are masked below).
+  auto load_stats = [&](int qt, float& l, float& dd) {
+    const int qq0 = qt * T::BRQ;
+    l = load1_bounded(Lh + qq0, n - qq0, l32);
+    dd = load1_bounded(Dh + qq0, n - qq0, l32);
+  };
+  float nl = 0.f, nd = 0.f;
+  // One 32-query stage: wait for it (loaded one stage ahead) and let every
+  // wave finish the previous one, load the next into the freed stage, then
+  // the wave's 32 x 32 block.  MASK: some query of the stage does not see
+  // some key of the workgroup, or the stage reaches past the end.
+  auto tile = [&](auto mask_tag, auto par_tag, int qt, int stage_rt, int qt_next) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    const int stage = (PAR >= 0) ? PAR : stage_rt;
+    ++nvis;
+    wait_dma();
+    __syncthreads();
+    const float cl = nl, cd = nd;
+    if (qt_next < n_qt) {
+      issue_stage(qt_next, stage ^ 1);
+      load_stats(qt_next, nl, nd);
+    }
+    const int so = stage * T::STAGE;
+    const int qq0 = qt * T::BRQ;
+    if (MASK && CAUSAL && qq0 + 31 + q_off < kw0) return;  // every query before every key
+    // S' = Q K^T - lse2 / c and dP' = dO V^T - D (M = query, N = key); the
+    // statistics enter as the last k-step.
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      const unsigned char* pa = smem + aK[ks] + q_minus_k + so;
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(smem + aK[ks]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + aK[ks] + T::ROW);
+      s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
+    }
+    s = mfma32(split_operand(cl * neg_inv_c, h), ones, s);
+    dp = mfma32(split_operand(-cd, h), ones, dp);
+    // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.  With MASK, P is
+    // zero for queries before this lane's key or past the end.
+    const int qlo = (CAUSAL ? key - q_off : 0) - qq0 - h * 4;
+    const int qhi = n - qq0 - h * 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(s[i] * c_log2);
+      if constexpr (MASK) {
+        const int qr = (i >> 2) * 8 + (i & 3);
+        if (qr < qlo || qr >= qhi) p = 0.f;
+      }
+      s[i] = p;
+      dp[i] = p * dp[i];
+    }
+    const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
+    const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
+    // dV^T += dO^T P and dK^T += Q^T dS (M = d, N = key, K = query).
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int pk = so + s2 * 16 * T::ROW;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const bf16x8 a_do = join_tr16(lds_read_tr16(smem + aT[db][0] + pk + T::S_DO),
+                                      lds_read_tr16(smem + aT[db][1] + pk + T::S_DO));
+        const bf16x8 a_q = join_tr16(lds_read_tr16(smem + aT[db][0] + pk),
+                                     lds_read_tr16(smem + aT[db][1] + pk));
+        adv[db] = mfma32(a_do, pf[s2], adv[db]);
+        adk[db] = mfma32(a_q, sf[s2], adk[db]);
+      }
+    }
+  };
+
+  using yes = std::true_type;
+  using no = std::false_type;
+  using par0 = std::integral_constant<int, 0>;
+  using par1 = std::integral_constant<int, 1>;
+  using par_rt = std::integral_constant<int, -1>;
+  if (qt_begin < n_qt) {
+    issue_stage(qt_begin, 0);
+    load_stats(qt_begin, nl, nd);
+    // Masked stages first (those holding a query that does not see the
+    // workgroup's last key: query + q_off < k0 + 255), unmasked stages in
+    // pairs with static stage parity (stage = (qt - qt_begin) & 1), the
+    // stage reaching past the end masked.
+    const int diag_last = k0 + T::BCK - 2 - q_off;  // last such query
+    const int head_end =
+        (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
+    const int full_end = n / T::BRQ;
+    int qt = qt_begin;
+#pragma unroll 1
+    for (; qt < head_end; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
+      tile(yes{}, par_rt{}, qt, (qt - qt_begin) & 1, qt + 1);
+    }
+    if (((qt - qt_begin) & 1) && qt < full_end) {
+      tile(no{}, par1{}, qt, 1, qt + 1);
+      qt = __builtin_amdgcn_readfirstlane(qt + 1);
+    }
+#pragma unroll 1
+    while (qt + 1 < full_end) {
+      tile(no{}, par0{}, qt, 0, qt + 1);
+      tile(no{}, par1{}, qt + 1, 1, qt + 2);
+      qt = __builtin_amdgcn_readfirstlane(qt + 2);
+    }
+#pragma unroll 1
+    for (; qt < n_qt; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
+      tile(yes{}, par_rt{}, qt, (qt - qt_begin) & 1, qt + 1);
+    }
+  }
+  // Every fill issued by this wave has landed (the K/V fill included, even
+  // when no query stage was visited) before the next tile's fills reuse LDS.
+  wait_dma();
+
+  if (key < nk) {
+    float* dkr = dK + hoff_k + (int64_t)key * D;
+    float* dvr = dV + hoff_k + (int64_t)key * D;
+    // D layout of dK^T / dV^T: lane = key, register i -> d = db*32 + (i/4)*8 + h*4 + i%4.
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = db * 32 + g * 8 + h * 4;
+        f32x4 xk, xv;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          xk[t] = adk[db][4 * g + t] * scale;
+          xv[t] = adv[db][4 * g + t];
+        }
+        *reinterpret_cast<f32x4*>(dkr + c) = xk;
+        *reinterpret_cast<f32x4*>(dvr + c) = xv;
+      }
+    }
+  }
+  if (visits != nullptr && w == 0 && lane == 0) {
+    visits[(int64_t)head * n_ktiles + kt] = nvis;
+  }
+  };
+
+  run_tile(kt_a);
+  if (CAUSAL && kt_b >= 0) {
+    __syncthreads();  // every wave is done with K, V and the stages
+    run_tile(kt_b);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
 template <int D, int NW_>
@@ -827,9 +1137,26 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
                        make_dropout(a.drop_t, a.seed_lo, a.seed_hi, a.q_off), a.visits_q);
 }
 
-// Block-sparse and/or dropout, or neither.
+template <bool CAUSAL>
+hipError_t dkdv256_t(const BwdArgs& a, hipStream_t s) {
+  using T = KV256Tile;
+  const int n_kt = (a.nk + T::BCK - 1) / T::BCK;
+  const int units = CAUSAL ? (n_kt + 1) / 2 : n_kt;
+  const int total = (int)(a.bh * units);
+  return launch_kernel(bwd_dkdv256_kernel<CAUSAL>, dim3(total), dim3(512), s,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (const bf16*)a.dout, (const float*)a.ws_d,
+                       (const float*)a.ws_lse2, a.dk, a.dv, a.n, a.nk, a.q_off,
+                       n_kt, total, a.scale * kLog2e, a.scale, a.visits_kv);
+}
+
+// d = 128 without mask or dropout: the 256-key kernel; otherwise 128 keys
+// per workgroup, with the block-sparse and/or dropout instances.
 template <int D>
 hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
+  if (D == 128 && !a.mask && a.drop_t == 0) {
+    return a.causal ? dkdv256_t<true>(a, s) : dkdv256_t<false>(a, s);
+  }
   if (a.mask) {
     if (a.drop_t > 0) {
       return a.causal ? dkdv_t<D, true, true, true>(a, s) : dkdv_t<D, false, true, true>(a, s);
@@ -857,7 +1184,12 @@ hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-void bwd_dkdv_tile_grid(int d, int* rows, int* cols) {
+void bwd_dkdv_tile_grid(int d, bool sparse, int* rows, int* cols) {
+  if (d == 128 && !sparse) {
+    *rows = KV256Tile::BRQ;
+    *cols = KV256Tile::BCK;
+    return;
+  }
   *rows = (d == 128) ? KVTile<128>::BRQ : KVTile<64>::BRQ;
   *cols = (d == 128) ? KVTile<128>::BCK : KVTile<64>::BCK;
 }

@@ -100,7 +100,7 @@ hipError_t launch_bwd_dq_f32(const BwdArgs& a, hipStream_t s);
 // the tiles it visits): forward query tile x key tile, dK/dV query stage x
 // key tile, dQ query tile x key tile.
 void fwd_bf16_tile_grid(int d, bool sparse, int* rows, int* cols);
-void bwd_dkdv_tile_grid(int d, int* rows, int* cols);
+void bwd_dkdv_tile_grid(int d, bool sparse, int* rows, int* cols);
 void bwd_dq_tile_grid(int d, bool sparse, int* rows, int* cols);
 
 // Library-owned scratch of the entry points that allocate nothing

@@ -22,7 +22,12 @@ void fwd_bf16_tile_grid(int d, bool sparse, int* rows, int* cols) {
   *rows = (d == 128 && !sparse) ? 256 : 128;
   *cols = (d == 128) ? 64 : 128;
 }
-void bwd_dkdv_tile_grid(int d, int* rows, int* cols) {
+void bwd_dkdv_tile_grid(int d, bool sparse, int* rows, int* cols) {
+  if (d == 128 && !sparse) {
+    *rows = 32;
+    *cols = 256;
+    return;
+  }
   *rows = (d == 128) ? 64 : 128;
   *cols = 128;
 }

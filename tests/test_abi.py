@@ -337,7 +337,8 @@ def test_tile_grid(lib):
     assert fa.fa_tile_grid(0, 128) == (256, 64)
     assert fa.fa_tile_grid(0, 64) == (128, 128)
     assert fa.fa_tile_grid(0, 128, sparse=True) == (128, 64)
-    assert fa.fa_tile_grid(1, 128) == (64, 128)
+    assert fa.fa_tile_grid(1, 128) == (32, 256)
+    assert fa.fa_tile_grid(1, 128, sparse=True) == (64, 128)
     assert fa.fa_tile_grid(1, 64) == (128, 128)
     assert fa.fa_tile_grid(2, 128) == (256, 64)
     assert fa.fa_tile_grid(2, 128, sparse=True) == (128, 64)
@@ -369,7 +370,7 @@ def test_tile_visits_validation(lib):
     assert bwdv(dt=F32) == FA_ERR_UNSUPPORTED
     assert bwdv(vkv=None) == FA_ERR_NULL
     assert bwdv(vq=P + 1) == FA_ERR_ALIGN
-    assert bwdv(nkv=2 * 8 - 1) == FA_ERR_ARG        # 2 heads x 8 key tiles
+    assert bwdv(nkv=2 * 4 - 1) == FA_ERR_ARG        # 2 heads x 4 key tiles of 256
     assert bwdv(nq=2 * 4 - 1) == FA_ERR_ARG         # 2 heads x 4 query tiles
     assert bwdv(ws=16) == FA_ERR_ARG
 

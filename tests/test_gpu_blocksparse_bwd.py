@@ -1,8 +1,10 @@
 """GPU parity of the block-sparse backward (fa_bwd_blocksparse) against the
 fp64 oracle's masked gradients, plus the identities the mask fixes: an
-all-ones mask is the dense backward (dK and dV bitwise: same tiles, same
-order; dQ to float32 rounding, as the dense causal dQ pass at d = 128 sums
-the keys of half its query tiles from the diagonal down), a diagonal mask is the dense backward of each diagonal chunk, and queries
+all-ones mask is the dense backward (bitwise at d = 64: same tiles, same
+order; at d = 128 the dense dQ pass sums the keys of half its causal query
+tiles from the diagonal down, float32 rounding apart, and the dense dK/dV
+pass is the 256-key kernel, whose statistics enter the products, so P and
+dS round to bf16 differently in a few elements), a diagonal mask is the dense backward of each diagonal chunk, and queries
 (keys) that see nothing get zero dQ (dK, dV)."""
 
 import math
@@ -86,10 +88,13 @@ def test_sparse_bwd_all_ones_is_dense(dev, d, causal):
     none = fa.fa_bwd_blocksparse(x["q"], x["k"], x["v"], o, x["do"], lse,
                                  None, scale=scale, causal=causal)
     for a, b, c, name in zip(dense, sp, none, ("dQ", "dK", "dV")):
+        err = float((a - b).abs().max())
         if name == "dQ" and causal and d == 128:
             # Same terms, another summation order: float32 rounding only.
-            err = float((a - b).abs().max())
             assert err <= 1e-5 * float(a.abs().max()), (name, err)
+        elif name != "dQ" and d == 128:
+            # Another kernel: bf16 rounding of P and dS in a few elements.
+            assert err <= 1e-2 * float(a.abs().max()), (name, err)
         else:
             assert torch.equal(a, b), f"all-ones mask {name} differs from dense"
         assert torch.equal(a, c), f"mask=None {name} differs from dense"

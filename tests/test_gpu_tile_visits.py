@@ -76,8 +76,9 @@ def test_fwd_causal_visits_half_the_tiles(dev, d):
 
 def test_metric_shape_visits(dev):
     # B=2 H=32 N=8192 d=128 causal: every head's count against the block
-    # rule, forward and both gradient passes; in units of 128 x 128 blocks
-    # the dK/dV pass visits exactly T(T+1)/2 (T = 64) per head.
+    # rule, forward and both gradient passes; in units of square blocks of
+    # its key-tile width c the dK/dV pass covers exactly T(T+1)/2 of them
+    # per head (T = N / c; its query stages divide c).
     B, H, N, d = 2, 32, 8192, 128
     x = gen(B, H, N, d, seed=3, sigma=0.5, with_do=True, dev=dev)
     o, lse, vf = fa.fa_fwd_tile_visits(x["q"], x["k"], x["v"], causal=True)
@@ -93,8 +94,9 @@ def test_metric_shape_visits(dev):
     assert (vf.sum(dim=2) == want_f).all(), "forward"
     assert (vkv.sum(dim=2) == want_kv).all(), "dK/dV pass"
     assert (vq.sum(dim=2) == want_q).all(), "dQ pass"
-    T = N // 128
-    assert want_kv * r1 * c1 == T * (T + 1) // 2 * 128 * 128
+    T = N // c1
+    assert c1 % r1 == 0
+    assert want_kv * r1 * c1 == T * (T + 1) // 2 * c1 * c1
     per_kt = _expected(N, r1, c1, True).sum(axis=0)
     assert np.array_equal(vkv[1, 31].cpu().numpy(), per_kt)
     print(f"  forward {want_f} tiles of {r0}x{c0}, dK/dV {want_kv} of "
