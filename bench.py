@@ -53,6 +53,7 @@ def fwd_flops(B, H, N, d, causal):
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fa_fwd_bf16.hip"],
     "bwd_dkdv_kernel": ["fa_bwd_bf16.hip"],
+    "bwd_dkdv256_kernel": ["fa_bwd_bf16.hip"],
     "bwd_dq_kernel": ["fa_bwd_bf16.hip"],
     "splitkv_bf16_kernel": ["fa_fwd_bf16.hip"],
     "bwd_blocksparse": ["fa_bwd_bf16.hip"],
@@ -630,9 +631,11 @@ def main():
     cands = [n for n in km if n != "bwd_preprocess"]
     dom = max(cands, key=lambda n: km[n])
     achieved = r["alg"][dom] / (km[dom] * 1e-3) / 1e12
+    # (At d = 128 without mask or dropout the dK/dV pass is the 256-key
+    # kernel.)
     kname = {"fwd": "fwd_bf16_kernel", "fwd_noncausal": "fwd_bf16_kernel",
-             "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
-             "bwd": "bwd_blocksparse"}[dom]
+             "bwd_dkdv": "bwd_dkdv256_kernel" if d == 128 else "bwd_dkdv_kernel",
+             "bwd_dq": "bwd_dq_kernel", "bwd": "bwd_blocksparse"}[dom]
     step_name = "fwd+bwd" if r["bwd_flops"] else "+".join(km)
     line = {
         "metric": METRIC,
