@@ -576,7 +576,10 @@ void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const float* Lh = ws_lse2 + (int64_t)head * n;
   const float* Dh = ws_d + (int64_t)head * n;
 
-  auto run_tile = [&](int kt) {
+  // One key tile; DOWN walks its query stages from the last one down
+  // instead of up from the first.
+  auto run_tile = [&](int kt, auto down_tag) {
+  constexpr bool DOWN = decltype(down_tag)::value;
   const int k0 = kt * T::BCK;
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + l32;
@@ -724,17 +727,44 @@ void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using par0 = std::integral_constant<int, 0>;
   using par1 = std::integral_constant<int, 1>;
   using par_rt = std::integral_constant<int, -1>;
-  if (qt_begin < n_qt) {
+  const int diag_last = k0 + T::BCK - 2 - q_off;  // last query that misses a key
+  const int head_end =
+      (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
+  const int full_end = n / T::BRQ;
+  if (DOWN && qt_begin < n_qt) {
+    // Highest stage first (stage = qt & 1): the stage reaching past the
+    // end, then the unmasked stages [head_end, full_end) in pairs with
+    // static parity (an odd stage first), then the masked stages down to
+    // qt_begin.
+    auto below = [&](int q) { return q - 1 >= qt_begin ? q - 1 : n_qt; };  // n_qt: none
+    int qt = n_qt - 1;
+    issue_stage(qt, qt & 1);
+    load_stats(qt, nl, nd);
+#pragma unroll 1
+    for (; qt >= qt_begin && qt >= full_end; qt = __builtin_amdgcn_readfirstlane(qt - 1)) {
+      tile(yes{}, par_rt{}, qt, qt & 1, below(qt));
+    }
+    if (qt >= head_end && qt >= qt_begin && !(qt & 1)) {
+      tile(no{}, par0{}, qt, 0, below(qt));
+      qt = __builtin_amdgcn_readfirstlane(qt - 1);
+    }
+#pragma unroll 1
+    while (qt - 1 >= head_end && qt - 1 >= qt_begin) {
+      tile(no{}, par1{}, qt, 1, qt - 1);
+      tile(no{}, par0{}, qt - 1, 0, below(qt - 1));
+      qt = __builtin_amdgcn_readfirstlane(qt - 2);
+    }
+#pragma unroll 1
+    for (; qt >= qt_begin; qt = __builtin_amdgcn_readfirstlane(qt - 1)) {
+      tile(yes{}, par_rt{}, qt, qt & 1, below(qt));
+    }
+  } else if (qt_begin < n_qt) {
     issue_stage(qt_begin, 0);
     load_stats(qt_begin, nl, nd);
     // Masked stages first (those holding a query that does not see the
     // workgroup's last key: query + q_off < k0 + 255), unmasked stages in
     // pairs with static stage parity (stage = (qt - qt_begin) & 1), the
     // stage reaching past the end masked.
-    const int diag_last = k0 + T::BCK - 2 - q_off;  // last such query
-    const int head_end =
-        (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
-    const int full_end = n / T::BRQ;
     int qt = qt_begin;
 #pragma unroll 1
     for (; qt < head_end; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
@@ -784,10 +814,17 @@ void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   };
 
-  run_tile(kt_a);
+  // Causal pairs: the first (long) tile walks down from the last query
+  // stage and the second walks up from its diagonal.  Tiles u and
+  // n_ktiles-1-u hold the same total work for every u, so at any moment the
+  // workgroups of a head read one of two query stages (the first tiles
+  // going down from the end, the second tiles going up from a common
+  // position), and their Q/dO reads share the XCD's L2 instead of spreading
+  // over the whole head.
+  run_tile(kt_a, std::integral_constant<bool, CAUSAL>{});
   if (CAUSAL && kt_b >= 0) {
     __syncthreads();  // every wave is done with K, V and the stages
-    run_tile(kt_b);
+    run_tile(kt_b, std::false_type{});
   }
 }
 
