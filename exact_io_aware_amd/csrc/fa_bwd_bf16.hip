@@ -382,9 +382,17 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using par0 = std::integral_constant<int, 0>;
   using par1 = std::integral_constant<int, 1>;
   using par_rt = std::integral_constant<int, -1>;
-  if constexpr (SPARSE) {
-    // Visited tiles in order, each in the masked form; the stage parity
-    // alternates over visited tiles.
+  // Masked tiles: under the causal rule those holding a query that does not
+  // see the workgroup's last key k0 + 127 (query + q_off < k0 + 127: they
+  // meet the diagonal), and the tile reaching past the end.
+  const int diag_last = k0 + T::BCK - 2 - q_off;  // last such query
+  const int head_end =
+      (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
+  const int full_end = n / T::BRQ;  // tiles before this are fully in range
+  if constexpr (SPARSE && D == 128) {
+    // Visited tiles in order, each in the masked form, the stage parity
+    // alternating at run time (a second, unmasked copy of the tile does not
+    // fit the registers at d = 128).
     int qt = next_on(qt_begin - 1);
     if (qt < n_qt) issue_stage(qt, 0);
     int stage = 0;
@@ -395,17 +403,33 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       qt = qn;
       stage ^= 1;
     }
+  } else if constexpr (SPARSE) {
+    // Visited tiles in order; the stage parity alternates over visited
+    // tiles, so they run in pairs with static parity, each in the masked
+    // form only where some element needs the mask.
+    auto visit = [&](auto par_tag, int qt, int qn) {
+      constexpr int PAR = decltype(par_tag)::value;
+      if (qt < head_end || qt >= full_end)
+        tile(yes{}, par_tag, qt, PAR, qn);
+      else
+        tile(no{}, par_tag, qt, PAR, qn);
+    };
+    int qt = next_on(qt_begin - 1);
+    if (qt < n_qt) issue_stage(qt, 0);
+#pragma unroll 1
+    while (qt < n_qt) {
+      int qn = next_on(qt);
+      visit(par0{}, qt, qn);
+      qt = qn;
+      if (qt >= n_qt) break;
+      qn = next_on(qt);
+      visit(par1{}, qt, qn);
+      qt = qn;
+    }
   } else if (qt_begin < n_qt) {
     issue_stage(qt_begin, 0);
-    // Masked tiles: under the causal rule those holding a query that does
-    // not see the workgroup's last key k0 + 127 (query + q_off < k0 + 127:
-    // they meet the diagonal), and the tile reaching past the end.
     // Unmasked tiles run in pairs with static stage parity (stage =
     // (qt - qt_begin) & 1).
-    const int diag_last = k0 + T::BCK - 2 - q_off;  // last such query
-    const int head_end =
-        (CAUSAL && diag_last >= 0) ? min(n_qt, diag_last / T::BRQ + 1) : qt_begin;
-    const int full_end = n / T::BRQ;  // tiles before this are fully in range
     int qt = qt_begin;
 #pragma unroll 1
     for (; qt < head_end; qt = __builtin_amdgcn_readfirstlane(qt + 1)) {
@@ -1045,9 +1069,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   using par0 = std::integral_constant<int, 0>;
   using par1 = std::integral_constant<int, 1>;
   using par_rt = std::integral_constant<int, -1>;
-  if constexpr (SPARSE) {
-    // Visited tiles in order, each in the masked form; the stage parity
-    // alternates over visited tiles.
+  if constexpr (SPARSE && D == 128) {
+    // Visited tiles in order, each in the masked form, the stage parity
+    // alternating at run time (a second, unmasked copy of the tile does not
+    // fit the registers at d = 128).
     int kt = next_on(-1);
     if (kt < kt_end) fill(kt, 0);
     int stage = 0;
@@ -1057,6 +1082,29 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       tile(yes{}, par_rt{}, kt, stage, kn);
       kt = kn;
       stage ^= 1;
+    }
+  } else if constexpr (SPARSE) {
+    // Visited tiles in order; the stage parity alternates over visited
+    // tiles, so they run in pairs with static parity, each in the masked
+    // form only where this wave's rows need the mask.
+    auto visit = [&](auto par_tag, int kt, int kn) {
+      constexpr int PAR = decltype(par_tag)::value;
+      if (needs_mask(kt))
+        tile(yes{}, par_tag, kt, PAR, kn);
+      else
+        tile(no{}, par_tag, kt, PAR, kn);
+    };
+    int kt = next_on(-1);
+    if (kt < kt_end) fill(kt, 0);
+#pragma unroll 1
+    while (kt < kt_end) {
+      int kn = next_on(kt);
+      visit(par0{}, kt, kn);
+      kt = kn;
+      if (kt >= kt_end) break;
+      kn = next_on(kt);
+      visit(par1{}, kt, kn);
+      kt = kn;
     }
   } else if constexpr (REV) {
     // Key tile kt sits in stage kt & 1 in either direction.  Downwards the
