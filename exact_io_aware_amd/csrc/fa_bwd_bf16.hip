@@ -404,26 +404,41 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       stage ^= 1;
     }
   } else if constexpr (SPARSE) {
-    // Visited tiles in order; the stage parity alternates over visited
-    // tiles, so they run in pairs with static parity, each in the masked
-    // form only where some element needs the mask.
-    auto visit = [&](auto par_tag, int qt, int qn) {
-      constexpr int PAR = decltype(par_tag)::value;
-      if (qt < head_end || qt >= full_end)
-        tile(yes{}, par_tag, qt, PAR, qn);
-      else
-        tile(no{}, par_tag, qt, PAR, qn);
-    };
+    // Visited tiles in order: those under the causal diagonal (masked),
+    // then the unmasked ones in pairs with static stage parity (the parity
+    // alternates over visited tiles), then the tile reaching past the end
+    // (masked).  Separate loops keep each tile body one basic block.
     int qt = next_on(qt_begin - 1);
     if (qt < n_qt) issue_stage(qt, 0);
+    int stage = 0;
 #pragma unroll 1
-    while (qt < n_qt) {
-      int qn = next_on(qt);
-      visit(par0{}, qt, qn);
+    for (; qt < n_qt && qt < head_end; stage ^= 1) {
+      const int qn = next_on(qt);
+      tile(yes{}, par_rt{}, qt, stage, qn);
       qt = qn;
-      if (qt >= n_qt) break;
+    }
+    if (stage && qt < full_end) {
+      const int qn = next_on(qt);
+      tile(no{}, par1{}, qt, 1, qn);
+      qt = qn;
+      stage = 0;
+    }
+#pragma unroll 1
+    while (qt < full_end) {
+      int qn = next_on(qt);
+      tile(no{}, par0{}, qt, 0, qn);
+      qt = qn;
+      stage = 1;
+      if (qt >= full_end) break;
       qn = next_on(qt);
-      visit(par1{}, qt, qn);
+      tile(no{}, par1{}, qt, 1, qn);
+      qt = qn;
+      stage = 0;
+    }
+#pragma unroll 1
+    for (; qt < n_qt; stage ^= 1) {
+      const int qn = next_on(qt);
+      tile(yes{}, par_rt{}, qt, stage, qn);
       qt = qn;
     }
   } else if (qt_begin < n_qt) {
@@ -1084,26 +1099,29 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       stage ^= 1;
     }
   } else if constexpr (SPARSE) {
-    // Visited tiles in order; the stage parity alternates over visited
-    // tiles, so they run in pairs with static parity, each in the masked
-    // form only where this wave's rows need the mask.
-    auto visit = [&](auto par_tag, int kt, int kn) {
-      constexpr int PAR = decltype(par_tag)::value;
-      if (needs_mask(kt))
-        tile(yes{}, par_tag, kt, PAR, kn);
-      else
-        tile(no{}, par_tag, kt, PAR, kn);
-    };
+    // Visited tiles in order: the unmasked ones in pairs with static stage
+    // parity (the parity alternates over visited tiles), then those needing
+    // this wave's element mask (they come last: keys increase along the
+    // visit order).  Separate loops keep each tile body one basic block.
     int kt = next_on(-1);
     if (kt < kt_end) fill(kt, 0);
+    int stage = 0;
 #pragma unroll 1
-    while (kt < kt_end) {
+    while (kt < kt_end && !needs_mask(kt)) {
       int kn = next_on(kt);
-      visit(par0{}, kt, kn);
+      tile(no{}, par0{}, kt, 0, kn);
       kt = kn;
-      if (kt >= kt_end) break;
+      stage = 1;
+      if (!(kt < kt_end && !needs_mask(kt))) break;
       kn = next_on(kt);
-      visit(par1{}, kt, kn);
+      tile(no{}, par1{}, kt, 1, kn);
+      kt = kn;
+      stage = 0;
+    }
+#pragma unroll 1
+    for (; kt < kt_end; stage ^= 1) {
+      const int kn = next_on(kt);
+      tile(yes{}, par_rt{}, kt, stage, kn);
       kt = kn;
     }
   } else if constexpr (REV) {
