@@ -717,35 +717,51 @@ void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int qq0 = qt * T::BRQ;
     if (MASK && CAUSAL && qq0 + 31 + q_off < kw0) return;  // every query before every key
     // S' = Q K^T - lse2 / c and dP' = dO V^T - D (M = query, N = key); the
-    // statistics enter as the last k-step.
+    // statistics enter as the last k-step.  The block runs as four groups of
+    // products, each next to the vector work that does not depend on it, so
+    // that a wave's exponentials and products overlap: S'; dP' beside
+    // P = exp2(c S') (two exponentials per product, held in place by empty
+    // asm statements, which the compiler otherwise moves behind all the
+    // products); dV beside dS = P dP'; dK.
     f32x16 s = zero16(), dp = zero16();
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
       const unsigned char* pa = smem + aK[ks] + q_minus_k + so;
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(smem + aK[ks]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + aK[ks] + T::ROW);
       s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
     }
     s = mfma32(split_operand(cl * neg_inv_c, h), ones, s);
-    dp = mfma32(split_operand(-cd, h), ones, dp);
+    __builtin_amdgcn_sched_barrier(0);
     // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.  With MASK, P is
     // zero for queries before this lane's key or past the end.
     const int qlo = (CAUSAL ? key - q_off : 0) - qq0 - h * 4;
     const int qhi = n - qq0 - h * 4;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    auto prob = [&](int i) {
       float p = fast_exp2(s[i] * c_log2);
       if constexpr (MASK) {
         const int qr = (i >> 2) * 8 + (i & 3);
         if (qr < qlo || qr >= qhi) p = 0.f;
       }
-      s[i] = p;
-      dp[i] = p * dp[i];
+      return p;
+    };
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      const unsigned char* pa = smem + aK[ks] + q_minus_k + so;
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + aK[ks] + T::ROW);
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
+      asm volatile("" : "+v"(dp));
+      float p0 = prob(2 * ks), p1 = prob(2 * ks + 1);
+      asm volatile("" : "+v"(p0), "+v"(p1));
+      s[2 * ks] = p0;
+      s[2 * ks + 1] = p1;
     }
+    dp = mfma32(split_operand(-cd, h), ones, dp);
     const bf16x8 pf[2] = {pack8(s, 0), pack8(s, 1)};
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P (M = d, N = key, K = query), beside dS = P dP'.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] = s[i] * dp[i];
     const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
-    // dV^T += dO^T P and dK^T += Q^T dS (M = d, N = key, K = query).
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int pk = so + s2 * 16 * T::ROW;
@@ -753,9 +769,18 @@ void bwd_dkdv256_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int db = 0; db < T::DB; ++db) {
         const bf16x8 a_do = join_tr16(lds_read_tr16(smem + aT[db][0] + pk + T::S_DO),
                                       lds_read_tr16(smem + aT[db][1] + pk + T::S_DO));
+        adv[db] = mfma32(a_do, pf[s2], adv[db]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dK^T += Q^T dS.
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int pk = so + s2 * 16 * T::ROW;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
         const bf16x8 a_q = join_tr16(lds_read_tr16(smem + aT[db][0] + pk),
                                      lds_read_tr16(smem + aT[db][1] + pk));
-        adv[db] = mfma32(a_do, pf[s2], adv[db]);
         adk[db] = mfma32(a_q, sf[s2], adk[db]);
       }
     }
@@ -903,6 +928,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
                    int block_n, Dropout drop, int* __restrict__ visits) {
   using T = QTile<D, NW>;
+  // (The dropout instances keep one block at a time: the pipeline does not
+  // fit their registers next to the random bytes.)
+  constexpr bool DQ_PIPE = !DROP;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE];
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1035,16 +1063,20 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // of block 0 (register i of block kb holds key kb*32 + (i/4)*8 + i%4
     // relative to it).
     const int lim = (CAUSAL ? min(qrow + q_off, nk - 1) : nk - 1) - kbase - h * 4;
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb) {
-      // S^T = K Q^T and dP^T = V dO^T (M = key, N = query).
-      f32x16 s = zero16(), dp = zero16();
+    // S^T = K Q^T and dP^T = V dO^T of 32-key block kb (M = key, N = query).
+    auto scores = [&](int kb, f32x16& s, f32x16& dp) {
+      s = zero16();
+      dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const unsigned char* pa = st + kb * 32 * T::ROW + aoff[ks];
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
       }
+    };
+    // dS^T of block kb from its S^T and dP^T, then dQ^T += K^T dS^T (M = d,
+    // N = query, K = key) with K^T from transpose reads of the K tile.
+    auto grad = [&](int kb, f32x16& s, f32x16& dp) {
       // Dropout: dS takes the kept and rescaled dP.
       uint32_t u[4];
       if constexpr (DROP) dropout_bytes_rowlane(drop, qrow, kbase + kb * 32, lane, u);
@@ -1060,8 +1092,6 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         dp[i] = p * (dpv - drow);
       }
       const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
-      // dQ^T += K^T dS^T (M = d, N = query, K = key); K^T from transpose
-      // reads of the K tile.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const unsigned char* pk = st + (kb * 2 + s2) * 16 * T::ROW;
@@ -1072,10 +1102,29 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           adq[db] = mfma32(a, sf[s2], adq[db]);
         }
       }
-      // One 32-key block at a time: its score registers are free before the
-      // next block's products, room the scheduler uses to keep two LDS
-      // operands in flight.
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (DQ_PIPE) {
+      // Software pipeline over the 32-key blocks: the products of block
+      // kb + 1 are issued together with block kb's vector work.
+      f32x16 s[2], dp[2];
+      scores(0, s[0], dp[0]);
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        if (kb + 1 < T::KB) scores(kb + 1, s[(kb + 1) & 1], dp[(kb + 1) & 1]);
+        grad(kb, s[kb & 1], dp[kb & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        f32x16 s, dp;
+        scores(kb, s, dp);
+        grad(kb, s, dp);
+        // One 32-key block at a time: its score registers are free before
+        // the next block's products, room the scheduler uses to keep two LDS
+        // operands in flight.
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
