@@ -1074,9 +1074,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
       }
     };
-    // dS^T of block kb from its S^T and dP^T, then dQ^T += K^T dS^T (M = d,
-    // N = query, K = key) with K^T from transpose reads of the K tile.
-    auto grad = [&](int kb, f32x16& s, f32x16& dp) {
+    // dS^T of block kb from its S^T and dP^T (bf16, the B operand of the dQ
+    // product).
+    auto dsv = [&](int kb, f32x16& s, f32x16& dp, bf16x8 (&sf)[2]) {
       // Dropout: dS takes the kept and rescaled dP.
       uint32_t u[4];
       if constexpr (DROP) dropout_bytes_rowlane(drop, qrow, kbase + kb * 32, lane, u);
@@ -1091,7 +1091,12 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           dpv = dropout_keep(u[i >> 2], i & 3, drop.t) ? dpv * drop.inv_keep : 0.f;
         dp[i] = p * (dpv - drow);
       }
-      const bf16x8 sf[2] = {pack8(dp, 0), pack8(dp, 1)};
+      sf[0] = pack8(dp, 0);
+      sf[1] = pack8(dp, 1);
+    };
+    // dQ^T += K^T dS^T of block kb (M = d, N = query, K = key); K^T from
+    // transpose reads of the K tile.
+    auto dq = [&](int kb, const bf16x8 (&sf)[2]) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const unsigned char* pk = st + (kb * 2 + s2) * 16 * T::ROW;
@@ -1104,22 +1109,27 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
     };
     if constexpr (DQ_PIPE) {
-      // Software pipeline over the 32-key blocks: the products of block
-      // kb + 1 are issued together with block kb's vector work.
+      // Software pipeline over the 32-key blocks: step kb issues the score
+      // products of block kb + 1 and the dQ products of block kb - 1 next to
+      // block kb's vector work.
       f32x16 s[2], dp[2];
+      bf16x8 sf[2][2];
       scores(0, s[0], dp[0]);
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
+      for (int kb = 0; kb <= T::KB; ++kb) {
         if (kb + 1 < T::KB) scores(kb + 1, s[(kb + 1) & 1], dp[(kb + 1) & 1]);
-        grad(kb, s[kb & 1], dp[kb & 1]);
+        if (kb >= 1) dq(kb - 1, sf[(kb - 1) & 1]);
+        if (kb < T::KB) dsv(kb, s[kb & 1], dp[kb & 1], sf[kb & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
         f32x16 s, dp;
+        bf16x8 sf[2];
         scores(kb, s, dp);
-        grad(kb, s, dp);
+        dsv(kb, s, dp, sf);
+        dq(kb, sf);
         // One 32-key block at a time: its score registers are free before
         // the next block's products, room the scheduler uses to keep two LDS
         // operands in flight.
