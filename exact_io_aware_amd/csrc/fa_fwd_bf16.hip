@@ -288,6 +288,48 @@ struct FwdWave {
     }
     l += rs;
   }
+  // The scores of the next tile (at sk, into s_next) and this tile's
+  // probabilities (probs above, without dropout) in one sequence: 16 / KS
+  // probabilities after each product, held in place by empty asm
+  // statements (the compiler otherwise issues all the products first, and
+  // the exponentials then wait behind them).  Same arithmetic, same order of
+  // the row sum.
+  __device__ __forceinline__ void scores_probs(const unsigned char* sk,
+                                               f32x16 (&s_next)[T::KB],
+                                               f32x16 (&s)[T::KB],
+                                               bf16x8 (&pf)[T::KK]) {
+    constexpr int PER = 16 / T::KS;  // probabilities per product
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      s_next[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            sk + kb * 32 * T::ROW + koff[ks]);
+        s_next[kb] = mfma32(a, qf[ks], s_next[kb]);
+        asm volatile("" : "+v"(s_next[kb]));
+        const int e0 = PER * (kb * T::KS + ks);  // elements e0 .. e0 + PER - 1 of s
+#pragma unroll
+        for (int j = 0; j < PER; j += 2) {
+          const int e = e0 + j;
+          float p0 = fast_exp2(fmaf(s[e >> 4][e & 15], c_log2, -m_use));
+          float p1 = fast_exp2(fmaf(s[e >> 4][(e & 15) + 1], c_log2, -m_use));
+          asm volatile("" : "+v"(p0), "+v"(p1));
+          rs += p0;
+          rs += p1;
+          s[e >> 4][e & 15] = p0;
+          s[e >> 4][(e & 15) + 1] = p1;
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      pf[2 * kb] = pack8(s[kb], 0);
+      pf[2 * kb + 1] = pack8(s[kb], 1);
+    }
+    l += rs;
+  }
   // O^T += V^T P^T for the V tile at sv.
   __device__ __forceinline__ void pv(const unsigned char* sv,
                                      const bf16x8 (&pf)[T::KK]) {
@@ -400,9 +442,13 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
         if (nxt2 < kt_end) fill.k(Kh, nxt2 * T::BC, n_keys, kbuf + kb_cur * T::K_BYTES);
         fill.v(Vh, nxt * T::BC, n_keys, vbuf + (kb_cur ^ 1) * T::K_BYTES);
       }
-      if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
       bf16x8 pf[T::KK];
-      wv.probs(s, pf, cur * T::BC);
+      if constexpr (NEXT && !DROP) {
+        wv.scores_probs(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next, s, pf);
+      } else {
+        if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
+        wv.probs(s, pf, cur * T::BC);
+      }
       wv.pv(vbuf + kb_cur * T::K_BYTES, pf);
       if constexpr (NEXT) {
         if constexpr (MASK_NEXT) wv.apply_mask(s_next, nxt * T::BC);
