@@ -288,12 +288,16 @@ struct FwdWave {
     }
     l += rs;
   }
+  // Whether the row sum of the probabilities is taken beside the PV
+  // products (pv_rowsum) rather than beside the score products, which
+  // carry the exponentials; at d = 64 that does not fit the registers.
+  static constexpr bool kSumBesidePV = (D == 128);
   // The scores of the next tile (at sk, into s_next) and this tile's
-  // probabilities (probs above, without dropout) in one sequence: 16 / KS
-  // probabilities after each product, held in place by empty asm
-  // statements (the compiler otherwise issues all the products first, and
-  // the exponentials then wait behind them).  Same arithmetic, same order of
-  // the row sum.
+  // probabilities (probs above, without dropout; the row sum here or in
+  // pv_rowsum, see kSumBesidePV) in one sequence: 16 / KS probabilities
+  // after each product, held in place by empty asm statements (the
+  // compiler otherwise issues all the products first, and the exponentials
+  // then wait behind them).  The fp32 probabilities stay in s.
   __device__ __forceinline__ void scores_probs(const unsigned char* sk,
                                                f32x16 (&s_next)[T::KB],
                                                f32x16 (&s)[T::KB],
@@ -316,8 +320,10 @@ struct FwdWave {
           float p0 = fast_exp2(fmaf(s[e >> 4][e & 15], c_log2, -m_use));
           float p1 = fast_exp2(fmaf(s[e >> 4][(e & 15) + 1], c_log2, -m_use));
           asm volatile("" : "+v"(p0), "+v"(p1));
-          rs += p0;
-          rs += p1;
+          if constexpr (!kSumBesidePV) {
+            rs += p0;
+            rs += p1;
+          }
           s[e >> 4][e & 15] = p0;
           s[e >> 4][(e & 15) + 1] = p1;
         }
@@ -327,6 +333,32 @@ struct FwdWave {
     for (int kb = 0; kb < T::KB; ++kb) {
       pf[2 * kb] = pack8(s[kb], 0);
       pf[2 * kb + 1] = pack8(s[kb], 1);
+    }
+    if constexpr (!kSumBesidePV) l += rs;
+  }
+  // pv below, with the row sum of the probabilities in s (fp32, left there
+  // by scores_probs) added into l beside the products, in the same order as
+  // probs adds them: the score product phase carries the exponentials, this
+  // one little vector work otherwise.
+  __device__ __forceinline__ void pv_rowsum(const unsigned char* sv,
+                                            const bf16x8 (&pf)[T::KK],
+                                            const f32x16 (&s)[T::KB]) {
+    constexpr int PER = (T::KB * 16) / (T::KK * T::DB);  // sums per product
+    static_assert(PER * T::KK * T::DB == T::KB * 16, "even split");
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) {
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const unsigned char* p = sv + kk * 16 * T::ROW + voff[db];
+        const bf16x8 a = join_tr16(lds_read_tr16(p), lds_read_tr16(p + 8 * T::ROW));
+        acc[db] = mfma32(a, pf[kk], acc[db]);
+        asm volatile("" : "+v"(acc[db]));
+        const int e0 = PER * (kk * T::DB + db);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) rs += s[(e0 + j) >> 4][(e0 + j) & 15];
+        asm volatile("" : "+v"(rs));
+      }
     }
     l += rs;
   }
@@ -449,7 +481,10 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
         if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
         wv.probs(s, pf, cur * T::BC);
       }
-      wv.pv(vbuf + kb_cur * T::K_BYTES, pf);
+      if constexpr (NEXT && !DROP && FwdWave<T, CAUSAL, DROP>::kSumBesidePV)
+        wv.pv_rowsum(vbuf + kb_cur * T::K_BYTES, pf, s);
+      else
+        wv.pv(vbuf + kb_cur * T::K_BYTES, pf);
       if constexpr (NEXT) {
         if constexpr (MASK_NEXT) wv.apply_mask(s_next, nxt * T::BC);
         wv.move_max(wv.tile_max(s_next));
