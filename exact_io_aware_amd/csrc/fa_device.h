@@ -245,6 +245,13 @@ inline Dropout make_dropout(int t, uint32_t seed_lo, uint32_t seed_hi,
                  (uint32_t)q_off};
 }
 
+// a ^ b ^ c in one instruction (gfx950's three-input bitwise operation
+// with truth table 0x96); the compiler emits two v_xor_b32 for the
+// expression.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // One Philox4x32-10 call: ten rounds of two 32 x 32 -> 64-bit products with
 // the published multipliers and a word permutation, the key advancing by the
 // published Weyl increments after each round.
@@ -254,8 +261,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&x)[4], uint32_t k0,
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)x[0] * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)x[2] * 0xCD9E8D57u;
-    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x[1] ^ k0;
-    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x[3] ^ k1;
+    const uint32_t y0 = xor3((uint32_t)(p1 >> 32), x[1], k0);
+    const uint32_t y2 = xor3((uint32_t)(p0 >> 32), x[3], k1);
     x[0] = y0;
     x[1] = (uint32_t)p1;
     x[2] = y2;
