@@ -317,8 +317,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       if (MASK && CAUSAL && qq0 + 31 + q_off < kw0) continue;  // every query before every key
       // Dropout: dV takes the kept probabilities (the 1/(1-p) factor is
       // applied at the end), dS the kept and rescaled dP.
-      uint32_t u[4];
-      if constexpr (DROP) dropout_bytes_keylane(drop, key, qq0, lane, u);
+      // (Dropout: the draw's ten rounds are spread between the products,
+      // held there by empty asm statements; the compiler otherwise puts them
+      // all in front.)
+      uint32_t u[4], x[4];
+      if constexpr (DROP) dropout_ctr_keylane(drop, key, qq0, lane, x);
       // S = Q K^T and dP = dO V^T (M = query, N = key), both operands from LDS.
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -328,7 +331,15 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         const bf16x8 vb = *reinterpret_cast<const bf16x8*>(smem + T::OFF_V + aK[ks]);
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), kb, s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::S_DO), vb, dp);
+        if constexpr (DROP) {
+          asm volatile("" : "+v"(s), "+v"(dp));
+#pragma unroll
+          for (int r = ks * 10 / T::KS; r < (ks + 1) * 10 / T::KS; ++r)
+            philox_round(x, drop.k0 + r * kWeyl0, drop.k1 + r * kWeyl1);
+          asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+        }
       }
+      if constexpr (DROP) dropout_finish_keylane(x, lane, u);
       // Register i holds query qq0 + (i/4)*8 + h*4 + i%4.  With MASK, P is
       // zero for queries before this lane's key or past the end: qrel is the
       // first visible query relative to qq0 + h*4, qend the end.
@@ -1064,22 +1075,32 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // relative to it).
     const int lim = (CAUSAL ? min(qrow + q_off, nk - 1) : nk - 1) - kbase - h * 4;
     // S^T = K Q^T and dP^T = V dO^T of 32-key block kb (M = key, N = query).
-    auto scores = [&](int kb, f32x16& s, f32x16& dp) {
+    // Dropout: u receives the block's random bytes, the draw's ten rounds
+    // spread between the products (held there by empty asm statements).
+    auto scores = [&](int kb, f32x16& s, f32x16& dp, uint32_t (&u)[4]) {
       s = zero16();
       dp = zero16();
+      if constexpr (DROP) dropout_ctr_rowlane(drop, qrow, kbase + kb * 32, lane, u);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const unsigned char* pa = st + kb * 32 * T::ROW + aoff[ks];
         s = mfma32(*reinterpret_cast<const bf16x8*>(pa), qf[ks], s);
         dp = mfma32(*reinterpret_cast<const bf16x8*>(pa + T::OFF_V), dof[ks], dp);
+        if constexpr (DROP) {
+          asm volatile("" : "+v"(s), "+v"(dp));
+#pragma unroll
+          for (int r = ks * 10 / T::KS; r < (ks + 1) * 10 / T::KS; ++r)
+            philox_round(u, drop.k0 + r * kWeyl0, drop.k1 + r * kWeyl1);
+          asm volatile("" : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]));
+        }
       }
+      if constexpr (DROP) quad_transpose(u, lane);
     };
     // dS^T of block kb from its S^T and dP^T (bf16, the B operand of the dQ
     // product).
-    auto dsv = [&](int kb, f32x16& s, f32x16& dp, bf16x8 (&sf)[2]) {
+    auto dsv = [&](int kb, f32x16& s, f32x16& dp, bf16x8 (&sf)[2],
+                   const uint32_t (&u)[4]) {
       // Dropout: dS takes the kept and rescaled dP.
-      uint32_t u[4];
-      if constexpr (DROP) dropout_bytes_rowlane(drop, qrow, kbase + kb * 32, lane, u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(s[i], c_log2, -lrow));
@@ -1114,12 +1135,13 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // block kb's vector work.
       f32x16 s[2], dp[2];
       bf16x8 sf[2][2];
-      scores(0, s[0], dp[0]);
+      uint32_t u[4];  // (no dropout here)
+      scores(0, s[0], dp[0], u);
 #pragma unroll
       for (int kb = 0; kb <= T::KB; ++kb) {
-        if (kb + 1 < T::KB) scores(kb + 1, s[(kb + 1) & 1], dp[(kb + 1) & 1]);
+        if (kb + 1 < T::KB) scores(kb + 1, s[(kb + 1) & 1], dp[(kb + 1) & 1], u);
         if (kb >= 1) dq(kb - 1, sf[(kb - 1) & 1]);
-        if (kb < T::KB) dsv(kb, s[kb & 1], dp[kb & 1], sf[kb & 1]);
+        if (kb < T::KB) dsv(kb, s[kb & 1], dp[kb & 1], sf[kb & 1], u);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -1127,8 +1149,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int kb = 0; kb < T::KB; ++kb) {
         f32x16 s, dp;
         bf16x8 sf[2];
-        scores(kb, s, dp);
-        dsv(kb, s, dp, sf);
+        uint32_t u[4];
+        scores(kb, s, dp, u);
+        dsv(kb, s, dp, sf, u);
         dq(kb, sf);
         // One 32-key block at a time: its score registers are free before
         // the next block's products, room the scheduler uses to keep two LDS

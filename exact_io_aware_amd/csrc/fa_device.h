@@ -252,24 +252,28 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
 
-// One Philox4x32-10 call: ten rounds of two 32 x 32 -> 64-bit products with
-// the published multipliers and a word permutation, the key advancing by the
-// published Weyl increments after each round.
+// One round of Philox4x32: two 32 x 32 -> 64-bit products with the
+// published multipliers and a word permutation, with the round's keys
+// (the seed words advanced by the published Weyl increments, kWeyl0/1 per
+// round).
+constexpr uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u;
+__device__ __forceinline__ void philox_round(uint32_t (&x)[4], uint32_t k0,
+                                             uint32_t k1) {
+  const uint64_t p0 = (uint64_t)x[0] * 0xD2511F53u;
+  const uint64_t p1 = (uint64_t)x[2] * 0xCD9E8D57u;
+  const uint32_t y0 = xor3((uint32_t)(p1 >> 32), x[1], k0);
+  const uint32_t y2 = xor3((uint32_t)(p0 >> 32), x[3], k1);
+  x[0] = y0;
+  x[1] = (uint32_t)p1;
+  x[2] = y2;
+  x[3] = (uint32_t)p0;
+}
+
+// One Philox4x32-10 call: ten rounds.
 __device__ __forceinline__ void philox4x32_10(uint32_t (&x)[4], uint32_t k0,
                                               uint32_t k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)x[0] * 0xD2511F53u;
-    const uint64_t p1 = (uint64_t)x[2] * 0xCD9E8D57u;
-    const uint32_t y0 = xor3((uint32_t)(p1 >> 32), x[1], k0);
-    const uint32_t y2 = xor3((uint32_t)(p0 >> 32), x[3], k1);
-    x[0] = y0;
-    x[1] = (uint32_t)p1;
-    x[2] = y2;
-    x[3] = (uint32_t)p0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
+  for (int r = 0; r < 10; ++r) philox_round(x, k0 + r * kWeyl0, k1 + r * kWeyl1);
 }
 
 // Transpose of a 4 x 4 matrix of words held by a quad of lanes (lanes 4m ..
@@ -298,16 +302,23 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&w)[4], int lane) {
 // 8 (r / 4) + 4 h + r % 4 relative to key0, h = lane / 32): word g of the
 // result holds, in byte t, the byte of key key0 + 8 g + 4 h + t.  row is this
 // lane's query; key0 is a multiple of 32, rows 4m .. 4m + 3 sit in the lanes
-// of one quad.
+// of one quad.  The counter alone (dropout_ctr_rowlane) lets a caller spread
+// the ten rounds (philox_round) between products and finish with
+// quad_transpose.
+__device__ __forceinline__ void dropout_ctr_rowlane(const Dropout& dr, int row,
+                                                    int key0, int lane,
+                                                    uint32_t (&x)[4]) {
+  const int h = (lane >> 5) & 1, q = lane & 3;
+  // this lane draws the 4 x 4 block of keys key0 + 8 q + 4 h ...
+  x[0] = (uint32_t)row >> 2;
+  x[1] = (uint32_t)(key0 + 8 * q + 4 * h) >> 2;
+  x[2] = dr.bh;
+  x[3] = dr.off;
+}
 __device__ __forceinline__ void dropout_bytes_rowlane(const Dropout& dr, int row,
                                                       int key0, int lane,
                                                       uint32_t (&out)[4]) {
-  const int h = (lane >> 5) & 1, q = lane & 3;
-  // this lane draws the 4 x 4 block of keys key0 + 8 q + 4 h ...
-  out[0] = (uint32_t)row >> 2;
-  out[1] = (uint32_t)(key0 + 8 * q + 4 * h) >> 2;
-  out[2] = dr.bh;
-  out[3] = dr.off;
+  dropout_ctr_rowlane(dr, row, key0, lane, out);
   philox4x32_10(out, dr.k0, dr.k1);
   // ... whose word q' belongs to row 4 (row >> 2) + q', the lane q' of the quad
   quad_transpose(out, lane);
@@ -316,25 +327,44 @@ __device__ __forceinline__ void dropout_bytes_rowlane(const Dropout& dr, int row
 // The same in the layout with lane = key (register r of the block holds
 // query 8 (r / 4) + 4 h + r % 4 relative to row0): word g of the result
 // holds, in byte t, the byte of query row0 + 8 g + 4 h + t and this lane's
-// key.  key is this lane's key; keys 4m .. 4m + 3 sit in one quad.
+// key.  key is this lane's key; keys 4m .. 4m + 3 sit in one quad.  Split
+// into the counter (dropout_ctr_keylane), the ten rounds (philox_round,
+// which a caller may spread between products) and the regrouping
+// (dropout_finish_keylane).
+__device__ __forceinline__ void dropout_ctr_keylane(const Dropout& dr, int key,
+                                                    int row0, int lane,
+                                                    uint32_t (&x)[4]) {
+  const int h = (lane >> 5) & 1, q = lane & 3;
+  x[0] = (uint32_t)(row0 + 8 * q + 4 * h) >> 2;
+  x[1] = (uint32_t)key >> 2;
+  x[2] = dr.bh;
+  x[3] = dr.off;
+}
+__device__ __forceinline__ void dropout_finish_keylane(const uint32_t (&x)[4],
+                                                       int lane,
+                                                       uint32_t (&out)[4]) {
+  // Word u of x belongs to query row0 + 8 q + 4 h + u and holds the four
+  // keys of the quad in its bytes; regroup so that word c holds key c's
+  // bytes of the four queries (byte u = query u): a 4 x 4 byte transpose,
+  // two byte permutations per word ...
+  const uint32_t lo01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t hi01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t lo23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+  // ... and hand word c to the lane of key c
+  quad_transpose(out, lane);
+}
 __device__ __forceinline__ void dropout_bytes_keylane(const Dropout& dr, int key,
                                                       int row0, int lane,
                                                       uint32_t (&out)[4]) {
-  const int h = (lane >> 5) & 1, q = lane & 3;
-  uint32_t x[4] = {(uint32_t)(row0 + 8 * q + 4 * h) >> 2, (uint32_t)key >> 2,
-                   dr.bh, dr.off};
+  uint32_t x[4];
+  dropout_ctr_keylane(dr, key, row0, lane, x);
   philox4x32_10(x, dr.k0, dr.k1);
-  // word u of x belongs to query row0 + 8 q + 4 h + u and holds the four
-  // keys of the quad in its bytes; regroup so that word c holds key c's
-  // bytes of the four queries (byte u = query u) ...
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int sh = 8 * c;
-    out[c] = ((x[0] >> sh) & 0xFFu) | (((x[1] >> sh) & 0xFFu) << 8) |
-             (((x[2] >> sh) & 0xFFu) << 16) | (((x[3] >> sh) & 0xFFu) << 24);
-  }
-  // ... and hand word c to the lane of key c
-  quad_transpose(out, lane);
+  dropout_finish_keylane(x, lane, out);
 }
 
 // Keep test of byte t of a word.
