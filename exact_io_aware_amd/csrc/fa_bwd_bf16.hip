@@ -16,15 +16,20 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
 //   dK = scale dS^T Q,  dQ = scale dS K.
 //
-// Three kernels, no atomics:
+// Three kernels, no atomics (fp32 atomic adds run at about one 4-byte add
+// per L2 channel per clock, too slow to fold dQ into the dK/dV pass):
 //   preprocess : D_i and lse_i * log2(e) per row (a streaming pass).
 //   dkdv       : a workgroup owns 128 keys (32 per wave and query half; K
-//                and V held in LDS for the workgroup's life) and sweeps the
-//                query tiles, accumulating dK^T and dV^T in registers; each
-//                is written once.
+//                and V held in LDS for the workgroup's life), or at d = 128
+//                without mask or dropout 256 keys (32 per wave), and sweeps
+//                the query tiles, accumulating dK^T and dV^T in registers;
+//                each is written once.
 //   dq         : a workgroup owns 128 or 256 queries (32 per wave, Q and dO
 //                held in registers) and sweeps the key tiles, accumulating
 //                dQ^T.
+// Within a wave the vector work of one group of products is issued beside
+// the next group's products (empty asm statements hold the order where the
+// compiler would otherwise issue all products first).
 // All contractions run on v_mfma_f32_32x32x16_bf16.  The dkdv pass computes
 // S = Q K^T so that each lane owns one key (the N index of the D layout); P
 // and dS then already have the B-operand layout for the contractions over

@@ -34,10 +34,12 @@
 //     contraction index is a dummy, so both sides only have to agree).
 //   * Software pipeline inside each wave: while the matrix cores compute
 //     the score tile of key tile j+1, the vector units turn tile j's scores
-//     into probabilities; while they compute tile j's PV product, the vector
-//     units mask and reduce tile j+1's scores to its row max.  K therefore
-//     runs one tile ahead of V: both are double-buffered in LDS and filled by
-//     direct global-to-LDS loads issued one tile ahead.
+//     into probabilities (two after each product, an order held by empty
+//     asm statements); while they compute tile j's PV product, the vector
+//     units add tile j's row sum (d = 128) and mask and reduce tile j+1's
+//     scores to its row max.  K therefore runs one tile ahead of V: both are
+//     double-buffered in LDS and filled by direct global-to-LDS loads issued
+//     one tile ahead.
 //   * The running max is only moved (and the accumulator rescaled) when a
 //     row's tile max exceeds it by more than 8 in log2 units; any reference
 //     value gives the same quotient, and probabilities stay below 2^8.
