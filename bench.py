@@ -60,14 +60,23 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """C++ source without comments and blank lines (so that editing a
+    comment does not mark the counters of an unchanged kernel as stale)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def kernel_source_hash(kernel):
-    """Hash of the sources a kernel is built from (its file + shared headers)."""
+    """Hash of the code a kernel is built from (its file + shared headers,
+    comments and blank lines removed)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_io_aware_amd", "csrc")
     files = KERNEL_SOURCES[kernel] + ["fa_device.h", "fa_internal.h"]
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
