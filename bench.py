@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one forward and one backward pass (preprocess, dK/dV pass, dQ
-pass) of bf16 causal attention at B=2, H=32, N=8192, d=128 on synthetic
-inputs already resident in device memory.  Prints one JSON line.
+One step = one forward and one backward pass (the dQ pass, which also forms
+the per-row statistics, then the dK/dV pass: the kernels of fa_bwd) of bf16
+causal attention at B=2, H=32, N=8192, d=128 on synthetic inputs already
+resident in device memory.  Prints one JSON line.
 
   value      whole-step throughput in TFLOP/s (forward 4*B*H*N^2*d/2 plus
              backward 2.5x that, divided by the measured step time)
@@ -145,9 +146,11 @@ def time_workload(name, steps, warmup, calib_mb=0):
     mask = workloads.workload_mask(w)
     mask_t = torch.from_numpy(mask).to(dev) if mask is not None else None
     has_bwd = "bwd" in w["passes"]
-    # The step's calls, each timed: dense backward workloads call the three
-    # backward passes one by one; the block-sparse workload its forward and
-    # its whole backward; forward-only workloads every causal mode they list.
+    # The step's calls, each timed: dense backward workloads call the two
+    # backward passes one by one, in fa_bwd's order (the dQ pass with the row
+    # statistics, then the dK/dV pass); the block-sparse workload its forward
+    # and its whole backward; forward-only workloads every causal mode they
+    # list.
     if mask_t is not None:
         calls = [("fwd", lambda: fa.fa_fwd_blocksparse(
                      q, k, v, mask_t, scale=scale, causal=causal, out=o, lse=lse)),
@@ -157,11 +160,11 @@ def time_workload(name, steps, warmup, calib_mb=0):
     elif has_bwd:
         calls = [("fwd", lambda: fa.fa_fwd(q, k, v, scale=scale, causal=causal,
                                            out=o, lse=lse)),
-                 ("bwd_preprocess", lambda: fa.fa_bwd_preprocess(o, do, lse, ws)),
+                 ("bwd_dq", lambda: fa.fa_bwd_dq_stats(q, k, v, o, do, lse, ws,
+                                                       dq, scale=scale,
+                                                       causal=causal)),
                  ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv,
-                                                     scale=scale, causal=causal)),
-                 ("bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, ws, dq, scale=scale,
-                                                 causal=causal))]
+                                                     scale=scale, causal=causal))]
     else:
         calls = [("fwd" if c else "fwd_noncausal",
                   (lambda c=c: fa.fa_fwd(q, k, v, scale=scale, causal=c, out=o,
@@ -203,8 +206,8 @@ def time_workload(name, steps, warmup, calib_mb=0):
     else:
         ff = fwd_flops(B, H, N, d, causal)
     alg = {"fwd": ff, "fwd_noncausal": fwd_flops(B, H, N, d, False),
-           "bwd": 2.5 * ff, "bwd_preprocess": 0.0,
-           "bwd_dkdv": 0.8 * 2.5 * ff, "bwd_dq": 0.2 * 2.5 * ff}
+           "bwd": 2.5 * ff, "bwd_dkdv": 0.8 * 2.5 * ff,
+           "bwd_dq": 0.2 * 2.5 * ff}
     alg = {n: alg[n] for n in names}
     return dict(w=w, B=B, H=H, N=N, d=d, causal=causal, ms_step=ms_step,
                 wall=wall, kern_ms=kern_ms, fwd_flops=ff,
@@ -637,8 +640,7 @@ def main():
     # The dominant kernel: the timed call with the most time (the block-sparse
     # backward's three kernels are timed as one call, fa_bwd_blocksparse,
     # reported as "bwd_blocksparse").
-    cands = [n for n in km if n != "bwd_preprocess"]
-    dom = max(cands, key=lambda n: km[n])
+    dom = max(km, key=lambda n: km[n])
     achieved = r["alg"][dom] / (km[dom] * 1e-3) / 1e12
     # (At d = 128 without mask or dropout the dK/dV pass is the 256-key
     # kernel.)

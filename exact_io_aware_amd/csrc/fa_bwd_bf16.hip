@@ -937,8 +937,9 @@ template <int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                   const float* __restrict__ ws_d,
-                   const float* __restrict__ ws_lse2, float* __restrict__ dQ,
+                   const bf16* __restrict__ O, const float* __restrict__ lse,
+                   float* __restrict__ ws_d, float* __restrict__ ws_lse2,
+                   float* __restrict__ dQ,
                    int n, int nk, int q_off, int n_qtiles, int total,
                    int bundle, float c_log2, float scale,
                    const uint8_t* __restrict__ mask, int mask_cols, int block_m,
@@ -992,8 +993,45 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     qf[ks] = as_bf16x8(load_row16(Q + hoff, qrow, n, D, ks * 16 + h * 8));
     dof[ks] = as_bf16x8(load_row16(dO + hoff, qrow, n, D, ks * 16 + h * 8));
   }
-  const float lrow = (qrow < n) ? ws_lse2[(int64_t)head * n + qrow] : INFINITY;
-  const float drow = (qrow < n) ? ws_d[(int64_t)head * n + qrow] : 0.f;
+  // The row statistics: with O given, computed here from O, dO and the
+  // forward's logsumexp and written to the workspace for the dK/dV pass
+  // (which then runs after this one), else read from the workspace.
+  float lrow, drow;
+  if (O != nullptr) {
+    // D = sum_c dO_c O_c in fp32, summed in the order of the streaming
+    // preprocess (one chain per 8 columns, then a pairwise tree over the
+    // chunks), so that both routes give the same bits: this lane holds the
+    // chunks 2ks + h, the tree's last level pairs the two half-waves.
+    float part[T::KS];
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      const u32x4 ov = load_row16(O + hoff, qrow, n, D, ks * 16 + h * 8);
+      const u32x4 dv = __builtin_bit_cast(u32x4, dof[ks]);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), acc);
+        acc = fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), acc);
+      }
+      part[ks] = acc;
+    }
+#pragma unroll
+    for (int st = T::KS / 2; st > 0; st >>= 1) {
+#pragma unroll
+      for (int ks = 0; ks < st; ++ks) part[ks] += part[ks + st];
+    }
+    const float dsum = sum_halves(part[0]);
+    const float L = (qrow < n) ? lse[(int64_t)head * n + qrow] : -INFINITY;
+    lrow = (L == -INFINITY) ? INFINITY : L * kLog2e;
+    drow = (qrow < n) ? dsum : 0.f;
+    if (h == 0 && qrow < n) {
+      ws_d[(int64_t)head * n + qrow] = drow;
+      ws_lse2[(int64_t)head * n + qrow] = lrow;
+    }
+  } else {
+    lrow = (qrow < n) ? ws_lse2[(int64_t)head * n + qrow] : INFINITY;
+    drow = (qrow < n) ? ws_d[(int64_t)head * n + qrow] : 0.f;
+  }
 
   f32x16 adq[T::DB];
 #pragma unroll
@@ -1310,7 +1348,7 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
 // d = 128 dense: 8-wave workgroups (256 query rows); block-sparse keeps 128
 // rows so that a workgroup lies in one 128-multiple block row of the mask.
 template <int D, bool CAUSAL, bool SPARSE, bool DROP>
-hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
+hipError_t dq_t(const BwdArgs& a, hipStream_t s, bool stats) {
   constexpr int NW = (D == 128 && !SPARSE) ? 8 : 4;
   using T = QTile<D, NW>;
   const int n_qt = (a.n + T::BRQ - 1) / T::BRQ;
@@ -1319,8 +1357,9 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   const int total = (int)(a.bh * units);
   return launch_kernel(bwd_dq_kernel<D, NW, CAUSAL, SPARSE, DROP>, dim3(total),
                        dim3(NW * 64), s, (const bf16*)a.q, (const bf16*)a.k,
-                       (const bf16*)a.v, (const bf16*)a.dout, (const float*)a.ws_d,
-                       (const float*)a.ws_lse2, a.dq, a.n, a.nk, a.q_off, n_qt,
+                       (const bf16*)a.v, (const bf16*)a.dout,
+                       stats ? (const bf16*)a.o : nullptr, stats ? a.lse : nullptr,
+                       a.ws_d, a.ws_lse2, a.dq, a.n, a.nk, a.q_off, n_qt,
                        total,
                        causal_bundle(n_qt, NW == 8 ? 1 : 2), a.scale * kLog2e,
                        a.scale, a.mask, a.mask_cols, a.block_m, a.block_n,
@@ -1359,17 +1398,17 @@ hipError_t dkdv_c(const BwdArgs& a, hipStream_t s) {
   return a.causal ? dkdv_t<D, true, false, false>(a, s) : dkdv_t<D, false, false, false>(a, s);
 }
 template <int D>
-hipError_t dq_c(const BwdArgs& a, hipStream_t s) {
+hipError_t dq_c(const BwdArgs& a, hipStream_t s, bool stats) {
   if (a.mask) {
     if (a.drop_t > 0) {
-      return a.causal ? dq_t<D, true, true, true>(a, s) : dq_t<D, false, true, true>(a, s);
+      return a.causal ? dq_t<D, true, true, true>(a, s, stats) : dq_t<D, false, true, true>(a, s, stats);
     }
-    return a.causal ? dq_t<D, true, true, false>(a, s) : dq_t<D, false, true, false>(a, s);
+    return a.causal ? dq_t<D, true, true, false>(a, s, stats) : dq_t<D, false, true, false>(a, s, stats);
   }
   if (a.drop_t > 0) {
-    return a.causal ? dq_t<D, true, false, true>(a, s) : dq_t<D, false, false, true>(a, s);
+    return a.causal ? dq_t<D, true, false, true>(a, s, stats) : dq_t<D, false, false, true>(a, s, stats);
   }
-  return a.causal ? dq_t<D, true, false, false>(a, s) : dq_t<D, false, false, false>(a, s);
+  return a.causal ? dq_t<D, true, false, false>(a, s, stats) : dq_t<D, false, false, false>(a, s, stats);
 }
 
 }  // namespace
@@ -1398,7 +1437,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  return a.d == 128 ? dq_c<128>(a, s) : dq_c<64>(a, s);
+  return a.d == 128 ? dq_c<128>(a, s, false) : dq_c<64>(a, s, false);
+}
+
+hipError_t launch_bwd_dq_stats(const BwdArgs& a, hipStream_t s) {
+  return a.d == 128 ? dq_c<128>(a, s, true) : dq_c<64>(a, s, true);
 }
 
 }  // namespace fa

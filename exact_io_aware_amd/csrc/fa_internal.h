@@ -91,6 +91,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+// The dQ pass that also computes the row statistics from o, dout and lse and
+// stores them in the workspace, in place of the preprocess (the dK/dV pass
+// then follows it).
+hipError_t launch_bwd_dq_stats(const BwdArgs& a, hipStream_t s);
 // float32 inputs (q, k, v, o, dout are float*).
 hipError_t launch_bwd_preprocess_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, hipStream_t s);

@@ -19,7 +19,8 @@ __all__ = [
     "FAError", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_splitkv",
     "fa_fwd_splitkv_chunks", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
     "fa_bwd_blocksparse", "fa_bwd_noalloc", "fa_bwd_preprocess",
-    "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes", "fa_status_str",
+    "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_bwd_workspace_bytes",
+    "fa_status_str",
     "fa_tile_grid", "fa_fwd_tile_visits", "fa_bwd_tile_visits",
     "fa_version", "library", "LIB_PATH",
 ]
@@ -71,6 +72,8 @@ def declare(lib):
         "fa_bwd_dkdv": [P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I,
                         P],
         "fa_bwd_dq": [P, P, P, P, P, P, SZ, I64, I64, I64, I64, I, F, I, P],
+        "fa_bwd_dq_stats": [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, I64, I,
+                            F, I, P],
         "fa_fwd_dropout": [P, P, P, P, P, I64, I64, I64, I64, I, F, I, F, U64,
                            P],
         "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I64, I64,
@@ -498,6 +501,21 @@ def fa_bwd_dq(q, k, v, do, workspace, dq, scale=None, causal=False):
             _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(workspace),
             ws_bytes, B, H, N, d, _dtype_code(q), _scale(scale, d),
             int(bool(causal)), _stream(q.device)))
+
+
+def fa_bwd_dq_stats(q, k, v, o, do, lse, workspace, dq, scale=None,
+                    causal=False):
+    """The preprocess and the dQ pass in one call: writes dq and the row
+    statistics into `workspace`, ready for fa_bwd_dkdv."""
+    B, H, N, d = _shape4(q, k, v, o, do)
+    _arg(lse, "lse", (B, H, N), torch.float32, q.device)
+    _arg(dq, "dq", q.shape, torch.float32, q.device)
+    workspace, ws_bytes = _ws_arg(workspace, q.device)
+    with torch.cuda.device(q.device):
+        _check(library().fa_bwd_dq_stats(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+            _ptr(workspace), ws_bytes, B, H, N, d, _dtype_code(q),
+            _scale(scale, d), int(bool(causal)), _stream(q.device)))
 
 
 def fa_tile_grid(pass_, d, sparse=False):

@@ -165,9 +165,12 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq,
  * rebuilt from q, k and the saved lse:
  *   D_i = sum_c dO_ic O_ic,  dV = P^T dO,  dP = dO V^T,
  *   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
- * Three kernels run in order on `stream`: a row pass computing D, a key-tile
- * pass producing dK and dV, and a query-tile pass producing dQ.  No atomics;
- * results are bitwise reproducible.
+ * Kernels run in order on `stream`.  FA_BF16: a query-tile pass producing dQ
+ * that also computes D and the base-2 logsumexp per row and leaves them in
+ * the workspace, then a key-tile pass producing dK and dV.  FA_F32: a row
+ * pass computing D, the key-tile pass, then the query-tile pass.  No
+ * atomics; results are bitwise reproducible and equal those of the three
+ * separate calls below.
  *
  * q, k, v, o, dout : inputs, B x H x N x d, dtype `dt` (o and lse from
  *                    fa_fwd on the same q, k, v, scale, causal).
@@ -335,14 +338,19 @@ fa_status fa_bwd_general(const void* q, const void* k, const void* v,
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
 /*
- * The three passes of fa_bwd as separate calls, for callers that time or
- * schedule them individually.  Calling preprocess, then dkdv and dq (in
- * either order, after preprocess) on the same workspace equals fa_bwd.
+ * The passes of fa_bwd as separate calls, for callers that time or schedule
+ * them individually.  Calling preprocess, then dkdv and dq (in either order,
+ * after preprocess) on the same workspace equals fa_bwd bitwise; so does
+ * calling dq_stats, then dkdv.
  *
  * fa_bwd_preprocess : reads o, dout, lse; writes the per-row D and the
  *                     base-2 logsumexp into `workspace`.
  * fa_bwd_dkdv       : reads q, k, v, dout and `workspace`; writes dk, dv.
  * fa_bwd_dq         : reads q, k, v, dout and `workspace`; writes dq.
+ * fa_bwd_dq_stats   : preprocess and dq in one: reads q, k, v, o, dout, lse;
+ *                     writes dq and the workspace rows preprocess writes
+ *                     (FA_BF16: one kernel, D_i formed from the O and dO rows
+ *                     the dQ pass holds; FA_F32: the two kernels).
  * Arguments they do not use may be NULL.  Validation as fa_bwd.
  */
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
@@ -359,6 +367,11 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v,
                     size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                     int64_t d, fa_dtype dt, float scale, int causal,
                     void* stream);
+fa_status fa_bwd_dq_stats(const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse,
+                          float* dq, void* workspace, size_t workspace_bytes,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          fa_dtype dt, float scale, int causal, void* stream);
 
 /*
  * Diagnostics: the tile schedule of the bf16 kernels.  The causal rule

@@ -14,6 +14,7 @@ hipError_t launch_fwd_f32(const FwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_preprocess(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_dkdv(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_dq(const BwdArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd_dq_stats(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_preprocess_f32(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_dkdv_f32(const BwdArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_dq_f32(const BwdArgs&, hipStream_t) { return hipSuccess; }

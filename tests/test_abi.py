@@ -156,6 +156,21 @@ def test_bwd_pass_validation(lib):
                          0, None) == FA_ERR_NULL
     assert lib.fa_bwd_dq(P, P, P, P, P, P, ws, 1, 1, 128, 64, BF16, -0.1, 0,
                          None) == FA_ERR_ARG
+    # dq_stats needs q, k, v, o, dout, lse, dq and the workspace
+    args = [P, P, P, P, P, P, P, P]
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        assert lib.fa_bwd_dq_stats(*a, ws, 1, 1, 128, 64, BF16, 0.125, 1,
+                                   None) == FA_ERR_NULL, i
+        assert lib.fa_bwd_dq_stats(*a, ws, 1, 1, 128, 64, F32, 0.125, 1,
+                                   None) == FA_ERR_NULL, i
+    assert lib.fa_bwd_dq_stats(*args, ws - 1, 1, 1, 128, 64, BF16, 0.125, 0,
+                               None) == FA_ERR_ARG
+    assert lib.fa_bwd_dq_stats(*args, ws, 1, 1, 128, 96, BF16, 0.125, 0,
+                               None) == FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_dq_stats(*args, ws, 1, 1, 128, 64, BF16, 0.0, 0,
+                               None) == FA_ERR_ARG
 
 
 def test_workspace_bytes(lib):

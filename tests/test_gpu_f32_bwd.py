@@ -107,6 +107,14 @@ def test_f32_bwd_passes_equal_fused_call(dev):
     fa.fa_bwd_dq(x["q"], x["k"], x["v"], x["do"], ws, dq2, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    # the combined preprocess + dQ call, then the dK/dV pass
+    ws.fill_(0x55)
+    dq3, dk3, dv3 = (torch.empty_like(t) for t in (dq, dk, dv))
+    fa.fa_bwd_dq_stats(x["q"], x["k"], x["v"], o, x["do"], lse, ws, dq3,
+                       causal=True)
+    fa.fa_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], ws, dk3, dv3, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
 
 
 def test_f32_bwd_repeatable(dev):

@@ -274,6 +274,41 @@ def test_bwd_passes_equal_fused_call(dev):
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dq_stats_equals_preprocess_and_dq(dev, d, causal):
+    # The dQ pass that forms the row statistics itself writes the same
+    # workspace bits as the preprocess and the same dQ as the dQ pass; then
+    # the dK/dV pass on it gives fa_bwd.  Ragged N, one row past a tile
+    # boundary; a row of -inf logsumexp (no key seen) maps to +inf.
+    B, H, N = 2, 3, 577
+    x = gen(B, H, N, d, seed=71 + d + causal, with_do=True, dev=dev)
+    o, lse = fa.fa_fwd(x["q"], x["k"], x["v"], causal=causal)
+    lse[1, 2, 5] = float("-inf")
+    nb = fa.fa_bwd_workspace_bytes(B, H, N, d)
+    ws1 = torch.full((nb,), 0x7f, dtype=torch.uint8, device=dev)
+    ws2 = torch.full((nb,), 0x55, dtype=torch.uint8, device=dev)
+    dq1, dq2, dk, dv = (torch.empty(x["q"].shape, dtype=torch.float32,
+                                    device=dev) for _ in range(4))
+    fa.fa_bwd_preprocess(o, x["do"], lse, ws1)
+    fa.fa_bwd_dq(x["q"], x["k"], x["v"], x["do"], ws1, dq1, causal=causal)
+    fa.fa_bwd_dq_stats(x["q"], x["k"], x["v"], o, x["do"], lse, ws2, dq2,
+                       causal=causal)
+    fa.fa_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], ws2, dk, dv, causal=causal)
+    ref = fa.fa_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=causal)
+    torch.cuda.synchronize()
+    # workspace: D over the rows, then (from a 64-row boundary) lse * log2(e)
+    rows = B * H * N
+    r64 = -(-rows // 64) * 64
+    st1, st2 = (w_.view(torch.float32) for w_ in (ws1, ws2))
+    for lo in (0, r64):
+        assert torch.equal(st1[lo:lo + rows], st2[lo:lo + rows])
+    assert float(st2[r64 + (1 * H + 2) * N + 5]) == float("inf")
+    assert torch.equal(dq1, dq2)
+    for a, b in zip((dq2, dk, dv), ref):
+        assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # worked examples, closed forms, determinism, streams
 # ---------------------------------------------------------------------------
