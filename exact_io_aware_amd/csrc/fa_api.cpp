@@ -236,6 +236,11 @@ fa_status splitkv_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
   int64_t sp;
   if (requested > 0) {
     sp = std::min(requested, n_kt);
+  } else if (Nq == 1) {
+    // One query row: one wave per chunk (the vector pass), about
+    // kSplitKvWaves waves in all, at least 8 tiles per chunk.
+    sp = std::max<int64_t>(1, fa::kSplitKvWaves / bh);
+    sp = std::min(sp, std::max<int64_t>(1, n_kt / 8));
   } else {
     sp = std::max<int64_t>(1, (2048 + base - 1) / base);
     sp = std::min(sp, std::max<int64_t>(1, n_kt / 8));

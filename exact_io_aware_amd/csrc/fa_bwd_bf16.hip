@@ -47,13 +47,6 @@
 namespace fa {
 namespace {
 
-__device__ __forceinline__ float bf16_lo(uint32_t u) {
-  return __uint_as_float(u << 16);
-}
-__device__ __forceinline__ float bf16_hi(uint32_t u) {
-  return __uint_as_float(u & 0xffff0000u);
-}
-
 // ---------------------------------------------------------------------------
 // preprocess: D_i = sum_c dO_ic * O_ic, lse2_i = lse_i * log2(e)
 // (+inf for rows whose forward saw no key, so that every rebuilt

@@ -84,6 +84,14 @@ __device__ __forceinline__ float fast_exp2(float x) {
 __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
 }
+// The two bf16 values of a 32-bit word (element 2i in the low half, 2i + 1
+// in the high half) as floats (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t u) {
+  return __uint_as_float(u << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t u) {
+  return __uint_as_float(u & 0xffff0000u);
+}
 
 // Chunk swizzle for a row-major bf16 tile with D columns that is read both
 // row-wise (16 consecutive rows, one 16-B chunk each, as an MFMA A operand)

@@ -730,6 +730,122 @@ void splitkv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   wv.store_partial(Opart + prow * D, LSEpart + prow);
 }
 
+// Decoding with a single query row: the chunk pass on the vector units.  A
+// 32-row matrix product would discard 31 of its rows here, and the pass is
+// bound by reading K and V once, so each wave streams one chunk with 16-byte
+// loads (D/8 lanes per key row, 64/(D/8) key slots per load) and keeps an
+// online-softmax state per key slot: reference max m (log2 units, moved only
+// when a score exceeds it by more than 8), exp-sum l, and the lane's 8 output
+// columns.  The slots are merged by the two-part rule at the end ([XYZ],
+// incremental softmax tracking) and the chunk's O (divided by its exp-sum)
+// and logsumexp are stored as the matrix-core chunk pass stores them.  One
+// wave per chunk, four chunks per workgroup.  Chunk c of a head takes the
+// key groups c, c + n_splits, c + 2 n_splits, ... (a group = the keys of one
+// round of loads), so that the waves of a head read neighbouring addresses
+// at the same time.
+template <int D>
+__global__ __launch_bounds__(256)
+void splitkv_vec_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                        const bf16* __restrict__ V, float* __restrict__ Opart,
+                        float* __restrict__ LSEpart, int nk, int n_splits,
+                        int n_chunks, int64_t bh, float c_log2) {
+  constexpr int LPK = D / 8;     // lanes per key row
+  constexpr int KPS = 64 / LPK;  // key slots per wave
+  constexpr int U = 4;           // loads of each of K and V in flight
+  constexpr int G = KPS * U;     // keys of one round of loads
+  constexpr float SLACK = 8.f;
+  const int chunk = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  if (chunk >= n_chunks) return;
+  const int lane = threadIdx.x & 63;
+  const int head = chunk / n_splits;
+  const int split = chunk % n_splits;
+  const int slot = lane / LPK;
+  const int c0 = (lane % LPK) * 8;
+
+  // This lane's 8 query columns, scaled to log2 units.
+  float qf[8];
+  {
+    const u32x4 qr = *reinterpret_cast<const u32x4*>(Q + (int64_t)head * D + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qf[2 * i] = bf16_lo(qr[i]) * c_log2;
+      qf[2 * i + 1] = bf16_hi(qr[i]) * c_log2;
+    }
+  }
+  const bf16* Kh = K + (int64_t)head * nk * D + c0;
+  const bf16* Vh = V + (int64_t)head * nk * D + c0;
+
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j0 = split * G; j0 < nk; j0 += n_splits * G) {
+    u32x4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = j0 + u * KPS + slot;
+      if (key < nk) {
+        kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D));
+        vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D));
+      } else {
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Score of this slot's key: 8 products per lane, summed over the
+      // LPK lanes of the key row.
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s = fmaf(qf[2 * i], bf16_lo(kr[u][i]), s);
+        s = fmaf(qf[2 * i + 1], bf16_hi(kr[u][i]), s);
+      }
+#pragma unroll
+      for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (j0 + u * KPS + slot >= nk) s = -INFINITY;
+      const bool move = s > m + SLACK;
+      if (__ballot(move)) {
+        const float m_new = move ? s : m;
+        const float alpha = move ? fast_exp2(m - m_new) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+        m = m_new;
+      }
+      const float p = fast_exp2(s - ((m == -INFINITY) ? 0.f : m));
+      l += p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(p, bf16_lo(vr[u][i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(p, bf16_hi(vr[u][i]), acc[2 * i + 1]);
+      }
+    }
+  }
+  // Merge the key slots (lanes that differ in the slot bits of their index).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    const float mx = fmaxf(m, m2);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    const float w1 = fast_exp2(m - mu), w2 = fast_exp2(m2 - mu);
+    l = l * w1 + l2 * w2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * w1 + __shfl_xor(acc[i], off) * w2;
+    m = mx;
+  }
+  const int64_t prow = (int64_t)split * bh + head;  // the chunk's row (one query)
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (slot == 0) {
+    float* orow = Opart + prow * D + c0;
+    *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  }
+  if (lane == 0) LSEpart[prow] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+}
+
 // Merge of the chunk results of one query row by the two-part softmax rule
 // ([XYZ], incremental softmax tracking), applied to all chunks at once: with
 // M = max_s lse_s and w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
@@ -770,13 +886,23 @@ void splitkv_merge_kernel(const float* __restrict__ Opart,
 
 template <int D, bool CAUSAL>
 hipError_t launch_splitkv_t(const SplitKvArgs& a, hipStream_t s) {
-  const int n_qtiles = (a.nq + 31) / 32;
-  const int total = (int)(a.bh * a.n_splits * n_qtiles);
-  hipError_t e = launch_kernel(
-      splitkv_bf16_kernel<D, CAUSAL>, dim3(total), dim3(64), s,
-      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.ws_o, a.ws_lse,
-      a.nq, a.nk, n_qtiles, a.n_splits, a.tiles_per_split, total, a.bh,
-      a.scale * kLog2e);
+  hipError_t e;
+  if (a.nq == 1) {
+    // One query row (which sees every key, causal or not): the vector pass.
+    const int chunks = (int)(a.bh * a.n_splits);
+    e = launch_kernel(splitkv_vec_kernel<D>, dim3((unsigned)((chunks + 3) / 4)),
+                      dim3(256), s, (const bf16*)a.q, (const bf16*)a.k,
+                      (const bf16*)a.v, a.ws_o, a.ws_lse, a.nk, a.n_splits,
+                      chunks, a.bh, a.scale * kLog2e);
+  } else {
+    const int n_qtiles = (a.nq + 31) / 32;
+    const int total = (int)(a.bh * a.n_splits * n_qtiles);
+    e = launch_kernel(
+        splitkv_bf16_kernel<D, CAUSAL>, dim3(total), dim3(64), s,
+        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.ws_o, a.ws_lse,
+        a.nq, a.nk, n_qtiles, a.n_splits, a.tiles_per_split, total, a.bh,
+        a.scale * kLog2e);
+  }
   if (e != hipSuccess) return e;
   const int64_t rows = a.bh * a.nq;
   constexpr int RPW = 256 / (D / 4);

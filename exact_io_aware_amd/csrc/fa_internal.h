@@ -67,6 +67,11 @@ struct BwdArgs {
 // keys, the keys cut into n_splits chunks of tiles_per_split tiles of
 // kSplitKvTile keys, every chunk non-empty.
 constexpr int kSplitKvTile = 32;
+// Waves of the one-query split-KV pass: two per SIMD of a 256-CU MI355X,
+// all resident at once.  Measured on B=16 H=32 Nk=16384 d=128: 1536-2048
+// waves read K and V fastest (6.8 TB/s); 1024 are too few (5.2 TB/s), and
+// 3072-8192 run 2-4% slower than 2048.
+constexpr int kSplitKvWaves = 2048;
 struct SplitKvArgs {
   const void* q;           // bh x nq x d
   const void* k;           // bh x nk x d

@@ -133,13 +133,17 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v,
  *              causal rule of fa_fwd.
  * n_splits   : >= 0.  0 picks the chunk count from the shape; a positive
  *              value caps it.  The count actually used is
- *              fa_fwd_splitkv_chunks(); every chunk holds at least one
- *              32-key tile.
+ *              fa_fwd_splitkv_chunks(), at most the number of 32-key tiles;
+ *              every chunk holds keys (whole 32-key tiles; with Nq = 1
+ *              interleaved groups of 16 (d = 128) or 32 (d = 64) keys).
  * workspace  : caller-owned device scratch of at least
  *              fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, n_splits)
  *              bytes, 16-byte aligned; contents on entry ignored.  Holds the
  *              chunk outputs (float32) and chunk logsumexps.
- * Two kernels run in order on `stream`: the chunk pass and the merge.
+ * Two kernels run in order on `stream`: the chunk pass and the merge.  With
+ * Nq = 1 the chunk pass runs on the vector units, one wave per chunk (a
+ * matrix product would waste 31 of its 32 rows; the pass is bound by reading
+ * K and V), and the automatic chunk count keeps every wave resident at once.
  * FA_BF16 only (FA_F32 returns FA_ERR_UNSUPPORTED); FA_ERR_ARG for negative
  * n_splits, a bad scale or a short workspace.
  */

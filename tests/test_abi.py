@@ -260,10 +260,17 @@ def test_splitkv_chunk_plan(lib):
     assert chunks(1, 1, 1, 1000, 128, 7) == 7     # 5 tiles each, 7 chunks
     assert chunks(1, 1, 1, 1000, 128, 1000) == 32
     assert chunks(1, 1, 1, 1000, 128, 1) == 1
-    # Automatic: at least 8 tiles per chunk, and no more chunks than needed
-    # for about 2048 workgroups.
+    # Automatic, several queries: at least 8 tiles per chunk, and no more
+    # chunks than needed for about 2048 workgroups.
+    assert chunks(8, 32, 4, 16384, 128, 0) == 8
+    assert chunks(1, 1, 40, 1000, 64, 0) == 4
+    # Automatic, one query (one wave per chunk): about 2048 chunks in all
+    # (2048 // (B*H) per head) with at least 8 tiles per chunk (24 heads of
+    # 200 tiles: 85 per head wanted, 25 allowed).
     assert chunks(1, 1, 1, 1000, 128, 0) == 4
     assert chunks(8, 32, 1, 16384, 128, 0) == 8
+    assert chunks(16, 32, 1, 16384, 128, 0) == 4
+    assert chunks(3, 8, 1, 6400, 64, 0) == 25
     assert chunks(64, 64, 1, 16384, 128, 0) == 1
     assert chunks(1, 1, 1, 16, 64, 0) == 1
     # workspace: chunks * rows * (d floats) + the logsumexps, 16-B rounded

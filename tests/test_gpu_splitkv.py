@@ -54,6 +54,12 @@ def _decode_case(dev, B, H, Nq, Nk, d, causal, splits, seed, heads=None):
     (64, 64, 128, True, 0),        # Nq = Nk: the square causal rule
     (100, 5000, 128, True, 7),
     (32, 2048, 64, False, 64),
+    # one query (the vector chunk pass): capped chunk counts, one tile per
+    # chunk with a 1-key last tile, and the automatic plan at a small B*H
+    (1, 777, 128, True, 5),
+    (1, 33, 64, False, 1000),
+    (1, 5000, 64, False, 0),
+    (1, 16384, 128, True, 0),
 ])
 def test_splitkv_shapes(dev, Nq, Nk, d, causal, splits):
     _decode_case(dev, 2, 3, Nq, Nk, d, causal, splits, seed=900 + Nq + Nk)
@@ -133,3 +139,41 @@ def test_splitkv_decode_workload(dev):
             w["scale"], True)
         compare(f"O[{b},{h}]", f64(o[b, h]), O)
         compare(f"LSE[{b},{h}]", f64(lse[b, h]), L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv_one_query_large_scores(dev, d):
+    # Scores spread over a wide range (Q and K scaled by 3: S has a standard
+    # deviation of about 9 at scale 1/sqrt(d)), so the running max moves
+    # many times inside each chunk.
+    B, H, Nk = 2, 2, 3000
+    x = workloads.make_decode_inputs(B, H, 1, Nk, d, seed=35, device=dev)
+    q = (x["q"].float() * 3).to(torch.bfloat16)
+    k = (x["k"].float() * 3).to(torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa.fa_fwd_splitkv(q, k, x["v"], scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            O, L = oracle.attention_decode_head(f64(q[b, h]), f64(k[b, h]),
+                                                f64(x["v"][b, h]), scale, True)
+            compare(f"O[{b},{h}]", f64(o[b, h]), O)
+            compare(f"LSE[{b},{h}]", f64(lse[b, h]), L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv_one_query_matches_general(dev, d):
+    # The vector chunk pass (one query) and the matrix-core forward with the
+    # query at the end of the sequence compute the same row; each agrees with
+    # the oracle, and they agree with each other to the bf16 bar.
+    B, H, Nk = 2, 3, 2500
+    x = workloads.make_decode_inputs(B, H, 1, Nk, d, seed=36, device=dev)
+    scale = 1 / math.sqrt(d)
+    o1, l1 = fa.fa_fwd_general(x["q"], x["k"], x["v"], scale=scale,
+                               causal=True)
+    for splits in (0, 1, 7):
+        o2, l2 = fa.fa_fwd_splitkv(x["q"], x["k"], x["v"], scale=scale,
+                                   causal=True, n_splits=splits)
+        torch.cuda.synchronize()
+        compare(f"O vector vs general, splits={splits}", f64(o2), f64(o1))
+        compare(f"LSE vector vs general, splits={splits}", f64(l2), f64(l1))
