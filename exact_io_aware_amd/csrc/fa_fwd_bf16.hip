@@ -691,7 +691,8 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t s) {
 // five of them fit a CU's LDS and keep enough K/V bytes in flight.  It writes
 // the chunk's normalised fp32 output and its logsumexp; splitkv_merge_kernel
 // combines the chunks.  The queries are the last nq of the nk positions, so
-// under the causal rule query i sees keys j <= nk - nq + i.
+// under the causal rule query i sees keys j <= nk - nq + i.  (A single query
+// row takes splitkv_vec_kernel below instead.)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void splitkv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
