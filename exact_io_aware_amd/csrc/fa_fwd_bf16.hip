@@ -39,7 +39,9 @@
 //     units add tile j's row sum (d = 128) and mask and reduce tile j+1's
 //     scores to its row max.  K therefore runs one tile ahead of V: both are
 //     double-buffered in LDS and filled by direct global-to-LDS loads issued
-//     one tile ahead.
+//     one tile ahead.  With dropout the next tile's score products carry
+//     this tile's random draws (the Philox rounds, spread between them)
+//     instead, and the probabilities follow.
 //   * The running max is only moved (and the accumulator rescaled) when a
 //     row's tile max exceeds it by more than 8 in log2 units; any reference
 //     value gives the same quotient, and probabilities stay below 2^8.
@@ -268,14 +270,19 @@ struct FwdWave {
   // every probability (the softmax statistics are those of P) while the
   // PV operand has the dropped ones zeroed; the 1/(1-p) factor is applied
   // with the final division.  kbase: the tile's first key.
+  template <bool DRAWN = false>
   __device__ __forceinline__ void probs(f32x16 (&s)[T::KB], bf16x8 (&pf)[T::KK],
-                                        int kbase) {
+                                        int kbase, const uint32_t (*drawn)[4] = nullptr) {
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       uint32_t u[4];
-      if constexpr (DROP)
+      if constexpr (DROP && DRAWN) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = drawn[kb][j];
+      } else if constexpr (DROP) {
         dropout_bytes_rowlane(dr, qrow, kbase + kb * 32, __lane_id(), u);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(s[kb][i], c_log2, -m_use));
@@ -337,6 +344,39 @@ struct FwdWave {
       pf[2 * kb + 1] = pack8(s[kb], 1);
     }
     if constexpr (!kSumBesidePV) l += rs;
+  }
+  // Dropout: the scores of the next tile (at sk, into s_next) with the
+  // random draws of the tile at kbase (this tile) spread between the
+  // products: each block's ten Philox rounds in order, held in place by
+  // empty asm statements.  u receives the tile's bytes for probs<true>.
+  __device__ __forceinline__ void scores_draw(const unsigned char* sk,
+                                              f32x16 (&s_next)[T::KB], int kbase,
+                                              uint32_t (&u)[T::KB][4]) {
+    constexpr int NM = T::KB * T::KS;  // products
+    constexpr int NU = T::KB * 10;     // rounds
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+      dropout_ctr_rowlane(dr, qrow, kbase + kb * 32, __lane_id(), u[kb]);
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      s_next[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            sk + kb * 32 * T::ROW + koff[ks]);
+        s_next[kb] = mfma32(a, qf[ks], s_next[kb]);
+        asm volatile("" : "+v"(s_next[kb]));
+        const int i = kb * T::KS + ks;
+#pragma unroll
+        for (int v = i * NU / NM; v < (i + 1) * NU / NM; ++v) {
+          const int b = v / 10, r = v % 10;
+          philox_round(u[b], dr.k0 + r * kWeyl0, dr.k1 + r * kWeyl1);
+          asm volatile("" : "+v"(u[b][0]), "+v"(u[b][1]), "+v"(u[b][2]), "+v"(u[b][3]));
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) quad_transpose(u[kb], __lane_id());
   }
   // pv below, with the row sum of the probabilities in s (fp32, left there
   // by scores_probs) added into l beside the products, in the same order as
@@ -479,6 +519,10 @@ __device__ __forceinline__ void key_loop(FwdWave<T, CAUSAL, DROP>& wv,
       bf16x8 pf[T::KK];
       if constexpr (NEXT && !DROP) {
         wv.scores_probs(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next, s, pf);
+      } else if constexpr (NEXT && DROP) {
+        uint32_t u[T::KB][4];
+        wv.scores_draw(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next, cur * T::BC, u);
+        wv.template probs<true>(s, pf, cur * T::BC, u);
       } else {
         if constexpr (NEXT) wv.scores(kbuf + (kb_cur ^ 1) * T::K_BYTES, s_next);
         wv.probs(s, pf, cur * T::BC);
