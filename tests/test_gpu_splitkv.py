@@ -60,6 +60,9 @@ def _decode_case(dev, B, H, Nq, Nk, d, causal, splits, seed, heads=None):
     (1, 33, 64, False, 1000),
     (1, 5000, 64, False, 0),
     (1, 16384, 128, True, 0),
+    (1, 16, 128, True, 0),         # one key group exactly
+    (1, 5, 128, False, 3),         # fewer keys than one group's slots
+    (1, 96, 64, False, 3),         # one group per chunk at d = 64
 ])
 def test_splitkv_shapes(dev, Nq, Nk, d, causal, splits):
     _decode_case(dev, 2, 3, Nq, Nk, d, causal, splits, seed=900 + Nq + Nk)
